@@ -1,0 +1,27 @@
+"""CPU oracle for the MXFP8 W8A8 linear layer.
+
+TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the CPU-baseline
+leg of the bench are the only callers. The product path (the HIP library and
+its Python binding) never imports, calls or links anything here, and nothing
+here imports the product package.
+
+Everything is plain numpy in float64. See ``oracle/mx_oracle.py`` for the
+definitions and the passages each function follows.
+"""
+
+from .mx_oracle import (  # noqa: F401
+    E4M3_MAX,
+    E4M3_EMAX,
+    GROUP,
+    bf16_round,
+    bf16_ulp,
+    dequantize_mx,
+    e4m3_decode,
+    e4m3_encode,
+    e8m0_decode,
+    gelu_tanh,
+    linear_ref,
+    mx_scale_code,
+    quantize_mx,
+    tolerance,
+)
