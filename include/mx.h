@@ -1,0 +1,119 @@
+/*
+ * mx.h - C ABI of the MXFP8 W8A8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The format is the one the model card "Wan2.2-I2V-A14B-Lightning · MXFP8
+ * (AutoRound OptRTN)" states in its section "Quantization Details": 8-bit
+ * weights and activations of data type mx_fp, group_size 32 along the
+ * reduction axis K, symmetric, activations quantized dynamically at run time;
+ * elements are FP8 E4M3, each group of 32 shares one E8M0 scale; the linear
+ * layers carry F16 biases. Accumulation is FP32 (the FP32-accumulation FP8
+ * mode of "Model Quantization Techniques", Conv3D mode table, which also fixes
+ * the E4M3 range at 448).
+ *
+ * Quantization rule for one group of 32 values (OCP MX conversion):
+ *   amax   = max |x_i|
+ *   e      = clamp(floor(log2 amax) - 8, -127, 127)   (amax = 0 gives -127)
+ *   scale  = E8M0 code e + 127
+ *   code_i = E4M3(x_i * 2^-e), round to nearest even after saturating to
+ *            +-448; the sign of zero is kept (-0 gives 0x80)
+ *   A group holding NaN or Inf gets scale 0xFF and every code 0x7F.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers; the caller allocates and frees
+ *     them. The library keeps no tensor state and allocates nothing per call.
+ *   - Layouts are row-major with K contiguous and no padding:
+ *       activations  x  bf16  [M][K]   (mx_quantize_act also takes a row pitch)
+ *       weights      w  fp32 or bf16 [N][K]  (nn.Linear orientation)
+ *       codes        q  uint8 [rows][K]      (E4M3)
+ *       scales       s  uint8 [rows][K/32]   (E8M0; group g covers K 32g..32g+31)
+ *       bias            f16 [N], or NULL for none
+ *       output       y  bf16  [M][N]
+ *   - `stream` is a hipStream_t (NULL is the default stream). Calls enqueue
+ *     work and return; faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are checked on the host before anything is launched. Every
+ *     call returns an mx_status; nothing is thrown and nothing aborts.
+ *     MX_ERR_INVALID_ARGUMENT: a required pointer is NULL; M, N < 0; K not a
+ *       positive multiple of 32; a pitch below K; x, q, w codes or y not
+ *       16-byte aligned (bias 2-byte aligned); an output overlapping an input;
+ *       an unknown epilogue or dtype.
+ *     MX_ERR_UNSUPPORTED: the current device is not gfx950 (or the environment
+ *       sets MX_FORCE_UNSUPPORTED=1).
+ *     MX_ERR_HIP: a HIP runtime call or a launch failed; mx_last_hip_error()
+ *       gives its hipError_t.
+ *     M = 0 or N = 0 is an empty call: MX_OK, nothing launched.
+ *   - Results are deterministic: the same inputs give the same bytes.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MX_ABI_VERSION 1
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_INVALID_ARGUMENT = 1,
+  MX_ERR_UNSUPPORTED = 2,
+  MX_ERR_HIP = 3
+} mx_status;
+
+/* Epilogue applied to acc + bias before the bf16 rounding. GELU is the tanh
+ * form, 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), the activation of
+ * the Wan2.2 feed-forward up-projection (ffn.net.0.proj). */
+typedef enum { MX_EPI_NONE = 0, MX_EPI_GELU_TANH = 1 } mx_epilogue;
+
+/* Element type of the weights handed to mx_quantize_weight. */
+typedef enum { MX_DT_BF16 = 0, MX_DT_F32 = 1 } mx_dtype;
+
+/* MX_ABI_VERSION of the built library. */
+int mx_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* mx_status_string(int status);
+
+/* hipError_t of the last MX_ERR_HIP returned on the calling thread (0 if none). */
+int mx_last_hip_error(void);
+
+/* Detail of the last non-OK status returned on the calling thread (static
+ * storage of that thread; "" if none). */
+const char* mx_last_error_message(void);
+
+/* Dynamic activation quantization ("act_dynamic", "act_group_size 32").
+ * x: bf16 [M][ldx] with ldx >= K and ldx % 8 == 0; q: uint8 [M][K];
+ * s: uint8 [M][K/32]. Bit-exact with the rule above. */
+int mx_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
+                    uint8_t* q, uint8_t* s, void* stream);
+
+/* Weight quantization, the same rule ("weights are stored as FP8 E4M3 with
+ * per-32 E8M0 scales"). w: [N][ldw] of type wdtype (MX_DT_F32 or MX_DT_BF16),
+ * ldw >= K, ldw * sizeof(element) % 16 == 0; q: uint8 [N][K]; s: uint8 [N][K/32]. */
+int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
+                       uint8_t* q, uint8_t* s, void* stream);
+
+/* The MXFP8 W8A8 linear with the activation quantization fused into the
+ * GEMM's prologue:
+ *   y[m][n] = bf16_rne( epi( sum_k xhat[m][k] * what[n][k] + f32(bias[n]) ) )
+ * with xhat the MX quantization of x (same rule as mx_quantize_act) and what
+ * the dequantized weights (wq, ws). Products are exact, sums are FP32.
+ * x: bf16 [M][K]; wq: uint8 [N][K]; ws: uint8 [N][K/32]; bias: f16 [N] or
+ * NULL; epilogue: mx_epilogue; y: bf16 [M][N]. */
+int mx_linear(const void* x, int64_t M, int64_t K,
+              const uint8_t* wq, const uint8_t* ws, int64_t N,
+              const void* bias, int epilogue, void* y, void* stream);
+
+/* The same linear on activations already quantized (e.g. by
+ * mx_quantize_act): xq: uint8 [M][K], xs: uint8 [M][K/32]. */
+int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                const uint8_t* wq, const uint8_t* ws, int64_t N,
+                const void* bias, int epilogue, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H */

@@ -1,0 +1,188 @@
+"""MXFP8 W8A8 linear layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/mx.h`` (same names). It only
+marshals arguments: torch tensors in, device pointers and the current HIP
+stream out; every step of the computation runs in the library's HIP kernels.
+If the built library ``libmxfp8.so`` is missing, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxfp8.so")
+
+MX_OK = 0
+MX_ERR_INVALID_ARGUMENT = 1
+MX_ERR_UNSUPPORTED = 2
+MX_ERR_HIP = 3
+MX_EPI_NONE = 0
+MX_EPI_GELU_TANH = 1
+MX_DT_BF16 = 0
+MX_DT_F32 = 1
+
+# Every symbol include/mx.h declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+SIGNATURES = {
+    "mx_abi_version": ([], _INT),
+    "mx_status_string": ([_INT], ctypes.c_char_p),
+    "mx_last_hip_error": ([], _INT),
+    "mx_last_error_message": ([], ctypes.c_char_p),
+    "mx_quantize_act": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
+    "mx_quantize_weight": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
+    "mx_linear": ([_P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
+    "mx_linear_q": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
+}
+
+
+class MXError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(message)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MXError(-1, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != MX_OK:
+        L = lib()
+        msg = L.mx_last_error_message().decode()
+        name = L.mx_status_string(status).decode()
+        raise MXError(status, f"{name}: {msg}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mx_abi_version():
+    return lib().mx_abi_version()
+
+
+def mx_status_string(status):
+    return lib().mx_status_string(status).decode()
+
+
+def mx_last_hip_error():
+    return lib().mx_last_hip_error()
+
+
+def mx_last_error_message():
+    return lib().mx_last_error_message().decode()
+
+
+def mx_quantize_act(x, q=None, s=None):
+    """bf16 [M, K] (rows may be strided) -> (codes uint8 [M, K], scales uint8 [M, K/32])."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    dev = x.device
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=dev) if s is None else s
+    _need(q, "q", torch.uint8, dev)
+    _need(s, "s", torch.uint8, dev)
+    ld = x.stride(0) if M > 1 else K
+    with torch.cuda.device(dev):
+        _check(lib().mx_quantize_act(_ptr(x), M, K, ld, _ptr(q), _ptr(s), _stream(dev)))
+    return q, s
+
+
+def mx_quantize_weight(w, q=None, s=None):
+    """fp32 or bf16 [N, K] -> (codes uint8 [N, K], scales uint8 [N, K/32])."""
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be 2-D with unit column stride")
+    dt = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}.get(w.dtype)
+    if dt is None:
+        raise TypeError(f"w must be float32 or bfloat16, got {w.dtype}")
+    N, K = w.shape
+    dev = w.device
+    q = torch.empty((N, K), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((N, K // 32), dtype=torch.uint8, device=dev) if s is None else s
+    _need(q, "q", torch.uint8, dev)
+    _need(s, "s", torch.uint8, dev)
+    ld = w.stride(0) if N > 1 else K
+    with torch.cuda.device(dev):
+        _check(lib().mx_quantize_weight(_ptr(w), dt, N, K, ld, _ptr(q), _ptr(s), _stream(dev)))
+    return q, s
+
+
+def _linear_common(M, K, wq, ws, bias, y, dev):
+    N = wq.shape[0]
+    _need(wq, "wq", torch.uint8, dev)
+    _need(ws, "ws", torch.uint8, dev)
+    if wq.shape != (N, K) or ws.shape != (N, K // 32):
+        raise ValueError(f"weights must be [N, {K}] codes and [N, {K // 32}] scales")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be f16 [N]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    return N, y
+
+
+def mx_linear(x, wq, ws, bias=None, gelu=False, y=None):
+    """y = bf16(epi(quant_mx(x) @ dequant(wq, ws)^T + bias)), activation
+    quantization fused into the GEMM. x: bf16 [M, K]."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev)
+    M, K = x.shape
+    N, y = _linear_common(M, K, wq, ws, bias, y, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(lib().mx_linear(_ptr(x), M, K, _ptr(wq), _ptr(ws), N, _ptr(bias), epi, _ptr(y), _stream(dev)))
+    return y
+
+
+def mx_linear_q(xq, xs, wq, ws, bias=None, gelu=False, y=None):
+    """The same linear on pre-quantized activations xq uint8 [M, K], xs uint8 [M, K/32]."""
+    dev = xq.device
+    _need(xq, "xq", torch.uint8, dev)
+    _need(xs, "xs", torch.uint8, dev)
+    M, K = xq.shape
+    if xs.shape != (M, K // 32):
+        raise ValueError("xs must be [M, K/32]")
+    N, y = _linear_common(M, K, wq, ws, bias, y, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_q(_ptr(xq), _ptr(xs), M, K, _ptr(wq), _ptr(ws), N, _ptr(bias), epi, _ptr(y), _stream(dev))
+        )
+    return y

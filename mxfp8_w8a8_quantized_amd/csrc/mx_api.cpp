@@ -1,0 +1,192 @@
+// C ABI of the MXFP8 W8A8 linear (include/mx.h): argument checks on the
+// host, the gfx950 check, and the launches. Every argument check runs before
+// any HIP call, so the error paths need no GPU.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "mx.h"
+#include "mx_internal.h"
+
+namespace {
+
+thread_local int t_last_hip = 0;
+thread_local char t_msg[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_msg, sizeof(t_msg), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  t_last_hip = (int)e;
+  return fail(MX_ERR_HIP, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+constexpr int64_t kMaxKN = int64_t(1) << 20;   // keeps in-tile byte offsets below 2^30
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+
+int check_k(int64_t K) {
+  if (K <= 0 || K % 32 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a positive multiple of 32", (long long)K);
+  if (K > kMaxKN) return fail(MX_ERR_UNSUPPORTED, "K = %lld exceeds the supported 2^20", (long long)K);
+  return MX_OK;
+}
+
+int check_rows(const char* name, int64_t R) {
+  if (R < 0) return fail(MX_ERR_INVALID_ARGUMENT, "%s = %lld is negative", name, (long long)R);
+  if (R > kMaxRows) return fail(MX_ERR_UNSUPPORTED, "%s = %lld exceeds the supported 2^30", name, (long long)R);
+  return MX_OK;
+}
+
+// Current device is gfx950 (cached per device), unless forced off.
+int check_device() {
+  const char* force = getenv("MX_FORCE_UNSUPPORTED");
+  if (force != nullptr && force[0] == '1') return fail(MX_ERR_UNSUPPORTED, "MX_FORCE_UNSUPPORTED=1");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::atomic<int> cache[64];  // 0 unknown, 1 gfx950, 2 other
+  if (dev < 0 || dev >= 64) return fail(MX_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  int c = cache[dev].load(std::memory_order_acquire);
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    c = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(c, std::memory_order_release);
+    if (c == 2) return fail(MX_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (c != 1) return fail(MX_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return MX_OK;
+}
+
+int finish(hipError_t e, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  t_msg[0] = '\0';
+  return MX_OK;
+}
+
+int check_linear_common(int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias,
+                        int epilogue, const void* y) {
+  int st;
+  if ((st = check_rows("M", M)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (N < 0) return fail(MX_ERR_INVALID_ARGUMENT, "N = %lld is negative", (long long)N);
+  if (N > kMaxKN) return fail(MX_ERR_UNSUPPORTED, "N = %lld exceeds the supported 2^20", (long long)N);
+  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH)
+    return fail(MX_ERR_INVALID_ARGUMENT, "unknown epilogue %d", epilogue);
+  if (M == 0 || N == 0) return MX_OK;
+  if (N % 16 != 0) return fail(MX_ERR_UNSUPPORTED, "N = %lld must be a multiple of 16", (long long)N);
+  if (wq == nullptr || ws == nullptr || y == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL weight or output pointer");
+  if (!aligned(wq, 16) || !aligned(y, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "wq and y must be 16-byte aligned");
+  if (bias != nullptr && !aligned(bias, 2)) return fail(MX_ERR_INVALID_ARGUMENT, "bias must be 2-byte aligned");
+  const uint64_t ybytes = (uint64_t)M * N * 2;
+  if (overlap(y, ybytes, wq, (uint64_t)N * K) || overlap(y, ybytes, ws, (uint64_t)N * (K / 32)) ||
+      overlap(y, ybytes, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MX_ABI_VERSION; }
+
+const char* mx_status_string(int status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_INVALID_ARGUMENT: return "MX_ERR_INVALID_ARGUMENT";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    case MX_ERR_HIP: return "MX_ERR_HIP";
+    default: return "MX_UNKNOWN_STATUS";
+  }
+}
+
+int mx_last_hip_error(void) { return t_last_hip; }
+
+const char* mx_last_error_message(void) { return t_msg; }
+
+int mx_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, uint8_t* s, void* stream) {
+  int st;
+  if ((st = check_rows("M", M)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
+  if (M == 0) return MX_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "x and q must be 16-byte aligned");
+  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2;
+  if (overlap(q, (uint64_t)M * K, x, xbytes) || overlap(s, (uint64_t)M * (K / 32), x, xbytes) ||
+      overlap(q, (uint64_t)M * K, s, (uint64_t)M * (K / 32)))
+    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_quantize(0, x, M, K, ldx, q, s, (hipStream_t)stream), "quantize launch");
+}
+
+int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q, uint8_t* s,
+                       void* stream) {
+  int st;
+  if (wdtype != MX_DT_BF16 && wdtype != MX_DT_F32) return fail(MX_ERR_INVALID_ARGUMENT, "unknown weight dtype %d", wdtype);
+  if ((st = check_rows("N", N)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  const int64_t es = wdtype == MX_DT_F32 ? 4 : 2;
+  if (ldw < K || (ldw * es) % 16 != 0)
+    return fail(MX_ERR_INVALID_ARGUMENT, "ldw = %lld must be >= K with 16-byte aligned rows", (long long)ldw);
+  if (N == 0) return MX_OK;
+  if (w == nullptr || q == nullptr || s == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(w, 16) || !aligned(q, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "w and q must be 16-byte aligned");
+  const uint64_t wbytes = ((uint64_t)(N - 1) * ldw + K) * es;
+  if (overlap(q, (uint64_t)N * K, w, wbytes) || overlap(s, (uint64_t)N * (K / 32), w, wbytes) ||
+      overlap(q, (uint64_t)N * K, s, (uint64_t)N * (K / 32)))
+    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_quantize(wdtype == MX_DT_F32 ? 1 : 0, w, N, K, ldw, q, s, (hipStream_t)stream),
+                "quantize launch");
+}
+
+int mx_linear(const void* x, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias,
+              int epilogue, void* y, void* stream) {
+  int st = check_linear_common(M, K, wq, ws, N, bias, epilogue, y);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (x == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x");
+  if (!aligned(x, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned");
+  if (overlap(y, (uint64_t)M * N * 2, x, (uint64_t)M * K * 2)) return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps x");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear(x, nullptr, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream), "linear launch");
+}
+
+int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws,
+                int64_t N, const void* bias, int epilogue, void* y, void* stream) {
+  int st = check_linear_common(M, K, wq, ws, N, bias, epilogue, y);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (xq == nullptr || xs == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL xq or xs");
+  if (!aligned(xq, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "xq must be 16-byte aligned");
+  const uint64_t yb = (uint64_t)M * N * 2;
+  if (overlap(y, yb, xq, (uint64_t)M * K) || overlap(y, yb, xs, (uint64_t)M * (K / 32)))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps xq or xs");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream), "linear launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,22 @@
+// Internal launchers shared by the C ABI layer (mx_api.cpp) and the kernels.
+// Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Elementwise MX quantization of `rows` rows of K elements (pitch ld
+// elements). kind: 0 = bf16 input, 1 = f32 input.
+hipError_t launch_quantize(int kind, const void* x, int64_t rows, int64_t K, int64_t ld,
+                           uint8_t* q, uint8_t* s, hipStream_t stream);
+
+// The block-scaled GEMM. When xs == nullptr, x is bf16 [M][K] and is
+// quantized in the prologue; otherwise x holds E4M3 codes [M][K] and xs the
+// E8M0 scales [M][K/32]. epi: 0 none, 1 GELU-tanh.
+hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
+                         const uint8_t* wq, const uint8_t* ws, int64_t N,
+                         const void* bias, int epi, void* y, hipStream_t stream);
+
+}  // namespace mx

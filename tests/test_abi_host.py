@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/mx.h declares, and rejects bad arguments before any HIP
+call (fake device addresses are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, mx
+
+HEADER = os.path.join(ROOT, "include", "mx.h")
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mx().lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mx().SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings(L):
+    assert L.mx_abi_version() == 1
+    assert L.mx_status_string(0) == b"MX_OK"
+    assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
+    assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
+    assert L.mx_status_string(3) == b"MX_ERR_HIP"
+    assert L.mx_status_string(42) == b"MX_UNKNOWN_STATUS"
+
+
+A = 0x10000  # aligned fake addresses
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+
+
+def qa(x=A, M=4, K=64, ld=64, q=B, s=C):
+    return mx().lib().mx_quantize_act(P(x), M, K, ld, P(q), P(s), P(0))
+
+
+def test_quantize_act_rejects_bad_arguments(L):
+    INV = 1
+    assert qa(K=33) == INV
+    assert qa(K=0) == INV
+    assert qa(K=-32) == INV
+    assert qa(M=-1) == INV
+    assert qa(ld=32) == INV  # ld < K
+    assert qa(ld=68) == INV  # rows not 16-byte aligned
+    assert qa(x=0) == INV
+    assert qa(q=0) == INV
+    assert qa(s=0) == INV
+    assert qa(x=A + 2) == INV  # misaligned
+    assert qa(q=B + 8) == INV
+    assert qa(q=A + 64) == INV  # q overlaps x
+    assert qa(s=B + 100) == INV  # s overlaps q
+    assert b"K" in L.mx_last_error_message() or len(L.mx_last_error_message()) > 0
+    assert qa(M=0) == 0  # empty call: nothing to do
+    assert qa(M=0, x=0, q=0, s=0) == 0
+
+
+def test_quantize_weight_rejects_bad_arguments(L):
+    f = L.mx_quantize_weight
+    assert f(P(A), 7, 4, 64, 64, P(B), P(C), P(0)) == 1  # dtype
+    assert f(P(A), 1, 4, 48, 48, P(B), P(C), P(0)) == 1  # K % 32
+    assert f(P(A), 1, 4, 64, 66, P(B), P(C), P(0)) == 1  # f32 rows not 16-byte aligned
+    assert f(P(A), 0, 4, 64, 68, P(B), P(C), P(0)) == 1  # bf16 rows not 16-byte aligned
+    assert f(P(0), 1, 4, 64, 64, P(B), P(C), P(0)) == 1
+    assert f(P(A), 1, 0, 64, 64, P(0), P(0), P(0)) == 0
+
+
+def lin(x=A, M=8, K=64, wq=B, ws=C, N=256, bias=0, epi=0, y=D):
+    return mx().lib().mx_linear(P(x), M, K, P(wq), P(ws), N, P(bias), epi, P(y), P(0))
+
+
+def test_linear_rejects_bad_arguments(L):
+    assert lin(K=40) == 1
+    assert lin(epi=5) == 1
+    assert lin(M=-3) == 1
+    assert lin(N=-16) == 1
+    assert lin(x=0) == 1
+    assert lin(wq=0) == 1
+    assert lin(y=0) == 1
+    assert lin(y=D + 4) == 1  # misaligned
+    assert lin(bias=A + 1) == 1  # odd bias address
+    assert lin(y=B) == 1  # y overlaps wq
+    assert lin(y=A) == 1  # y overlaps x
+    assert lin(N=264) == 2  # N % 16: outside the kernel's tiling
+    assert lin(K=1 << 21) == 2
+    assert lin(M=0) == 0
+    assert lin(N=0) == 0
+    q = L.mx_linear_q
+    assert q(P(A), P(0), 8, 64, P(B), P(C), 256, P(0), 0, P(D), P(0)) == 1  # NULL xs
+    assert q(P(A), P(C + 64), 8, 64, P(B), P(C), 256, P(0), 0, P(A), P(0)) == 1  # y overlaps xq
+
+
+def test_forced_unsupported_path(L, monkeypatch):
+    monkeypatch.setenv("MX_FORCE_UNSUPPORTED", "1")
+    assert qa() == 2
+    assert lin() == 2
+    assert b"MX_FORCE_UNSUPPORTED" in L.mx_last_error_message()
+
+
+def test_oracle_and_product_share_no_code():
+    pkg = os.path.join(ROOT, "mxfp8_w8a8_quantized_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), fn
+                assert "oracle/" not in text, fn
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith(".py"):
+            text = open(os.path.join(ROOT, "oracle", fn)).read()
+            assert "mxfp8_w8a8_quantized_amd" not in text, fn
+            assert "synth" not in text, fn
