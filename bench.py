@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 W8A8 linear on one MI355X.
+
+One step = one call of the hot path on the fused self-attention q|k|v
+projection of Wan2.2-A14B over the full video latent: M = 75348 tokens,
+K = 5120, N = 15360, bf16 activations quantized to MXFP8 inside the GEMM,
+E4M3 weights with E8M0 scales (quantized once, before timing), f16 bias,
+bf16 output. Throughput counts the algorithmic 2*M*N*K FLOP.
+
+Prints ONE JSON line. Besides the contract fields it carries:
+  roofline      the dominant kernel (the fused linear) against the dense
+                MXFP8 MFMA peak, timed per launch with HIP events on the
+                launch stream; `traffic` comes from the committed rocprofv3
+                counter summary when it was taken on the current kernel
+                sources, else null;
+  cpu_baseline  the float64 CPU oracle timed on a bounded row sample of the
+                same inputs;
+  extra         the quantize-then-GEMM path (mx_quantize_act + mx_linear_q)
+                and the quantizers' bandwidth.
+
+--profile-copy runs only a device copy of known size (for calibrating the
+HBM byte counters) and --no-cpu-baseline skips the oracle leg.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 W8A8 linear TFLOP/s incl. act-quant, M=75348 K=5120; % of MXFP8 peak"
+WORKLOAD = "qkv_75348x5120x15360"
+PEAK_MXFP8_TFLOPS = 5000.0  # MI355X dense MXFP8/FP8 MFMA peak
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_fused_qkv_75348x5120x15360.json")
+KERNEL_SOURCES = ["mx_gemm.hip", "mx_device.h"]
+CPU_SAMPLE_ROWS = 8192
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mxfp8_w8a8_quantized_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile-copy", action="store_true", help="run only a 1 GiB device copy")
+    return ap.parse_args()
+
+
+def timed(torch, fn, steps, warmup):
+    """Runs fn warmup times, then steps times; returns (total ms, per-launch ms list)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    wq, ws = oracle.quantize_mx(w_cpu.double().numpy())  # offline, like the GPU's weights
+    xr = x_cpu[:rows].double().numpy()
+    b = b_cpu.double().numpy()
+    t0 = time.perf_counter()
+    xq, xs = oracle.quantize_mx(xr)
+    y, S = oracle.linear_ref(xq, xs, wq, ws, bias=b)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(y).all()
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": 2.0 * rows * K * N / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} token rows x all {N} outputs (K={K}): float64 activation quantization + "
+        f"dequantized GEMM with its sum|a||b| bound, {dt:.1f} s; FLOP counted as 2*rows*N*K",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(
+            f"bench.py measures one GPU only (got --gpus {args.gpus}); the linear shards over tokens with no "
+            "exchange, so multi-GPU throughput is N times the one-GPU figure by construction and is not measured.",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import mxfp8_w8a8_quantized_amd as mx
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.profile_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+
+    if not os.path.exists(mx.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+
+    shape = synth.CONFIGS[WORKLOAD][0]
+    M, K, N = shape.M, shape.K, shape.N
+    x_cpu = synth.make_activation(M, K, seed=0)
+    w_cpu = synth.make_weight(N, K, seed=0)
+    b_cpu = synth.make_bias(N, seed=0)
+    x = x_cpu.to(dev)
+    w = w_cpu.to(dev)
+    bias = b_cpu.to(dev)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    # Weight quantization happens once, outside the step (weights are stored
+    # quantized); timed here only for the quantizer's bandwidth.
+    _, wq_ms = timed(torch, lambda: mx.mx_quantize_weight(w, wq, ws), 3, 1)
+    del w
+
+    step = lambda: mx.mx_linear(x, wq, ws, bias, y=y)  # noqa: E731
+    total_ms, launch_ms = timed(torch, step, args.steps, args.warmup)
+    flop = 2.0 * M * N * K
+    ms_per_step = total_ms / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    avg_launch = sum(launch_ms) / len(launch_ms)
+    achieved = flop / (avg_launch * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD,
+            "M": M,
+            "K": K,
+            "N": N,
+            "act_quant": "fused in GEMM prologue",
+            "epilogue": "f16 bias, bf16 out",
+            "pct_of_mxfp8_peak": round(100.0 * value / PEAK_MXFP8_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_MXFP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MXFP8_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "linear_kernel<fused>",
+            "launch_ms": round(avg_launch, 4),
+        },
+    }
+
+    if not args.no_extra:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        _, q_ms = timed(torch, lambda: mx.mx_quantize_act(x, xq, xs), 10, 2)
+        _, l_ms = timed(torch, lambda: mx.mx_linear_q(xq, xs, wq, ws, bias, y=y), 10, 2)
+        qa = sum(q_ms) / len(q_ms)
+        lq = sum(l_ms) / len(l_ms)
+        act_bytes = M * K * (2 + 1 + 1 / 32)
+        w_bytes = N * K * (4 + 1 + 1 / 32)
+        wqa = sum(wq_ms) / len(wq_ms)
+        out["extra"] = {
+            "quantize_act_ms": round(qa, 4),
+            "quantize_act_GBps": round(act_bytes / (qa * 1e-3) / 1e9, 1),
+            "quantize_act_hbm_frac": round(act_bytes / (qa * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "linear_prequant_ms": round(lq, 4),
+            "two_pass_TFLOPs": round(flop / ((qa + lq) * 1e-3) / 1e12, 2),
+            "quantize_weight_f32_ms": round(wqa, 4),
+            "quantize_weight_GBps": round(w_bytes / (wqa * 1e-3) / 1e9, 1),
+        }
+        del xq, xs
+
+    if not args.no_cpu_baseline:
+        del x, y
+        out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, b_cpu, CPU_SAMPLE_ROWS)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
