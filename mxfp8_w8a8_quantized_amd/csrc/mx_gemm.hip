@@ -57,6 +57,10 @@ constexpr int kDropOffset = 1 << 30;  // beyond every resource: the store is dro
 #define MX_STORE_AUX 2
 #endif
 constexpr int kStoreAux = MX_STORE_AUX;  // cache policy of output stores (2: non-temporal)
+#ifndef MX_LOAD_AUX
+#define MX_LOAD_AUX 0
+#endif
+constexpr int kLoadAux = MX_LOAD_AUX;  // cache policy of the direct operand loads
 
 struct Params {
   const uint8_t* x;   // bf16 tokens (fused) or E4M3 codes
@@ -440,8 +444,8 @@ __device__ __forceinline__ void issue_loads(const Src& S, uint8_t* st, int kk, b
     const int q = wave * 8 + u;
     const int soff = 8 * q * S.K + dbase;
     const int vo = (u & 1) ? S.voff1 : S.voff;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(S.w, (lds_ptr)(st + OFF_W + q * 1024), 16, vo, soff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(S.x, (lds_ptr)(st + OFF_X + q * 1024), 16, vo, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(S.w, (lds_ptr)(st + OFF_W + q * 1024), 16, vo, soff, 0, kLoadAux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(S.x, (lds_ptr)(st + OFF_X + q * 1024), 16, vo, soff, 0, kLoadAux);
   }
 }
 
@@ -475,9 +479,14 @@ __device__ __forceinline__ void interleave_half_step() {
   });
 }
 
-// Slot-wise emission of half-step 4: slot i issues MFMA i on the current
-// fragments, then LDS read i of the next fragments, then global load i of the
-// stage after next, pinned in that order.
+// Slot-wise emission of half-step 4: slot i issues global loads
+// kLoadsPerSlot*i .. of the stage after next, then MFMA i on the current
+// fragments, then LDS read i of the next fragments, pinned in that order.
+// Front-loading the global loads gives them the longest time to land.
+#ifndef MX_LOADS_PER_SLOT
+#define MX_LOADS_PER_SLOT 4
+#endif
+constexpr int kLoadsPerSlot = MX_LOADS_PER_SLOT;
 struct FragAddr {
   const uint8_t* a;  // weight rows of this lane in the stage (chunk offsets applied below)
   const uint8_t* b;
@@ -532,9 +541,9 @@ __device__ __forceinline__ void load_piece(const Src& S, uint8_t* st, int kk, bo
     const int soff = 8 * q * S.K + dbase;
     const int vo = (u & 1) ? S.voff1 : S.voff;
     if constexpr ((I & 1) == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.w, (lds_ptr)(st + OFF_W + q * 1024), 16, vo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.w, (lds_ptr)(st + OFF_W + q * 1024), 16, vo, soff, 0, kLoadAux);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.x, (lds_ptr)(st + OFF_X + q * 1024), 16, vo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.x, (lds_ptr)(st + OFF_X + q * 1024), 16, vo, soff, 0, kLoadAux);
   } else {
     const int sbase = valid ? kk * 4 : kDropOffset;
     if constexpr (I == 16)
@@ -657,9 +666,11 @@ __global__ __launch_bounds__(NT, 1) void linear_prequant_kernel(Params p) {
       const bool valid = k + 2 < nk;
       static_for<0, 18>([&](auto I) {
         constexpr int i = decltype(I)::value;
+        static_for<i * kLoadsPerSlot, (i + 1) * kLoadsPerSlot < 18 ? (i + 1) * kLoadsPerSlot : 18>([&](auto L) {
+          load_piece<decltype(L)::value>(S, st, k + 2, valid, wave, swn, sxn);
+        });
         if constexpr (i < 16) mfma_piece<i>(acc, F1);
         read_piece<i>(F0, A);
-        load_piece<i>(S, st, k + 2, valid, wave, swn, sxn);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
@@ -673,6 +684,231 @@ __global__ __launch_bounds__(NT, 1) void linear_prequant_kernel(Params p) {
   __builtin_amdgcn_s_barrier();
   store_tile<EPI>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
+
+// ---------------------------------------------------------------------------
+// Ring pipeline. The TA -> L1 -> L2 path of a CU sustains about 64 B/clk; a
+// 256 x 256 tile needs 32 B/clk at MFMA peak. The two-stage loop above can
+// only refill a stage after its mid-iteration barrier, so it pushes a whole
+// stage (64 KB) through in half an iteration, fills the address FIFO and
+// blocks the waves' instruction issue (MFMAs included). Here K advances in
+// half-steps of 64 through a ring of 4 regions, each freed as soon as its
+// fragments have been read, so the refill of half-step j+4 is issued at the
+// start of half-step j and loads stream at the average rate with three
+// half-steps (about 3000 cycles) to land:
+//
+//   half-step j:  wait for this wave's loads of j+1, barrier;
+//                 issue the loads of j+4 into region j % 4;
+//                 16 MFMAs on fragments of j (registers), interleaved with
+//                 the LDS reads of the fragments of j+1 (region (j+1) % 4).
+//
+// Scales travel by LDS DMA too (one dword = 4 groups per row per 128-K step,
+// a 4-slot ring), so no load result passes through registers and every wait
+// is explicit. Each lane reads its 4 scale bytes per operand with byte loads
+// and hands them to the MFMA with op_sel 0.
+namespace ring {
+
+constexpr int R_W = 0;          // weight codes: 256 rows x 64 B, chunk c of row r at c ^ ((r >> 2) & 3)
+constexpr int R_X = 16384;      // token codes, same layout
+constexpr int REGION = 32768;
+constexpr int OFF_SC = 4 * REGION;       // scale slots: [slot 0..3][W 1 KB | X 1 KB], row-major dwords
+constexpr int SLOT = 2048;
+constexpr int LDS = OFF_SC + 4 * SLOT;   // 136 KB
+
+struct Frags {
+  i32x8 a[4];
+  i32x8 b[4];
+  int sa[4];  // scale byte (bits 0..7) of frag f
+  int sb[4];
+};
+
+struct Src {
+  __amdgpu_buffer_rsrc_t w, x, ws, xs;
+  int K, G32;
+  int voff;   // lane part of a code DMA offset: row L/4, logical chunk (L%4) ^ (L/16)
+  int soff;   // lane part of a scale DMA offset: row L
+};
+
+// Load number I of half-step j into region j % 4: I = 0..7 code DMAs of
+// 1 KB (16 rows x 64 B; W and X alternating, 4 each per wave), I = 8, 9 (even
+// j only) the scale DMAs of its 128-K step into slot (j/2) % 4, 256 B each.
+// Past the last half-step the offsets fall outside the resources: the DMAs
+// then write zeros and touch no memory.
+template <int I>
+__device__ __forceinline__ void load_piece(const Src& S, uint8_t* smem, int j, int nh, int wave) {
+  const bool valid = j < nh;
+  if constexpr (I < 8) {
+    uint8_t* reg = smem + (j & 3) * REGION;
+    const int q = wave * 4 + I / 2;  // 16-row block
+    const int so = 16 * q * S.K + (valid ? j * 64 : kDropOffset);
+    if constexpr ((I & 1) == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.w, (lds_ptr)(reg + R_W + q * 1024), 16, S.voff, so, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.x, (lds_ptr)(reg + R_X + q * 1024), 16, S.voff, so, 0, 0);
+  } else {
+    uint8_t* slot = smem + OFF_SC + ((j >> 1) & 3) * SLOT;
+    const int so = 64 * wave * S.G32 + (valid ? (j >> 1) * 4 : kDropOffset);
+    if constexpr (I == 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.ws, (lds_ptr)(slot + wave * 256), 4, S.soff, so, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(S.xs, (lds_ptr)(slot + 1024 + wave * 256), 4, S.soff, so, 0, 0);
+  }
+}
+
+template <bool EVEN>
+__device__ __forceinline__ void load_half(const Src& S, uint8_t* smem, int j, int nh, int wave) {
+  static_for<0, EVEN ? 10 : 8>([&](auto I) { load_piece<decltype(I)::value>(S, smem, j, nh, wave); });
+}
+
+struct FragAddr {
+  const uint8_t* a;
+  const uint8_t* b;
+  int c0, c1;
+  const uint8_t* sa;
+  const uint8_t* sb;
+};
+
+// Fragments of half-step j: lane l, frag f reads row base + 32 f + l%32,
+// K bytes [16 (l/32), +16) and [32 + 16 (l/32), +16) of the 64, and the scale
+// byte of group 2 (j % 2) + l/32 of its 128-K step.
+__device__ __forceinline__ FragAddr frag_addr(const uint8_t* smem, int j, int wn, int wm, int lane) {
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int sw = (r32 >> 2) & 3;
+  const uint8_t* reg = smem + (j & 3) * REGION;
+  FragAddr A;
+  A.a = reg + R_W + (wn * 128 + r32) * 64;
+  A.b = reg + R_X + (wm * 128 + r32) * 64;
+  A.c0 = (hi ^ sw) << 4;
+  A.c1 = ((2 + hi) ^ sw) << 4;
+  const uint8_t* slot = smem + OFF_SC + ((j >> 1) & 3) * SLOT;
+  const int g = 2 * (j & 1) + hi;
+  A.sa = slot + (wn * 128 + r32) * 4 + g;
+  A.sb = slot + 1024 + (wm * 128 + r32) * 4 + g;
+  return A;
+}
+
+// LDS read number i (0..23) of a fragment set: 16 code halves, 8 scale bytes.
+template <int I>
+__device__ __forceinline__ void read_piece(Frags& F, const FragAddr& A) {
+  if constexpr (I < 16) {
+    constexpr int f = I / 4, part = I % 4;
+    const uint8_t* base = (part < 2 ? A.a : A.b) + 32 * f * 64;
+    const i32x4 v = *(const i32x4*)(base + ((part & 1) ? A.c1 : A.c0));
+    i32x8& d = part < 2 ? F.a[f] : F.b[f];
+    if constexpr ((part & 1) == 0) {
+      d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    } else {
+      d[4] = v[0]; d[5] = v[1]; d[6] = v[2]; d[7] = v[3];
+    }
+  } else if constexpr (I < 20) {
+    F.sa[I - 16] = *(const uint8_t*)(A.sa + 32 * (I - 16) * 4);
+  } else {
+    F.sb[I - 20] = *(const uint8_t*)(A.sb + 32 * (I - 20) * 4);
+  }
+}
+
+template <int I>
+__device__ __forceinline__ void mfma_piece(f32x16 (&acc)[4][4], const Frags& F) {
+  constexpr int i = I / 4, j = I % 4;
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, F.sa[i], 0, F.sb[j]);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): written as asm because the compiler's own
+// waitcnt pass relaxes the builtin form to the counts it tracks, and the
+// lgkmcnt(0) here is what keeps another wave's DMA refill from overtaking
+// this wave's last reads of the region being refilled.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N));
+}
+
+// One half-step j (parity EVEN): barrier, loads of j+4, MFMAs of j on `cur`
+// interleaved with the reads of j+1 into `nxt`.
+template <bool EVEN>
+__device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
+                                          int j, int nh, int wave, int wn, int wm, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<18>();  // loads of j+1 landed (those of j+2, j+3 may fly)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const FragAddr A = frag_addr(smem, j + 1, wn, wm, lane);
+  constexpr int NL = EVEN ? 10 : 8;  // loads of half-step j+4 (same parity as j)
+  static_for<0, 16>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < NL) load_piece<i>(S, smem, j + 4, nh, wave);
+    mfma_piece<i>(acc, cur);
+    read_piece<i>(nxt, A);
+    if constexpr (i < 8) read_piece<16 + i>(nxt, A);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void linear_prequant_ring(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int K = p.K, G32 = K >> 5, nh = K / 64;  // nh is even (K % 128 == 0)
+  const int rows_m = min(p.M - m0, BM);
+  const int rows_n = min(p.N - n0, BN);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+
+  Src S;
+  S.w = make_rsrc(p.wq + (size_t)n0 * K, (uint32_t)(rows_n * K));
+  S.ws = make_rsrc(p.ws + (size_t)n0 * G32, (uint32_t)(rows_n * G32));
+  S.x = make_rsrc(p.x + (size_t)m0 * K, (uint32_t)(rows_m * K));
+  S.xs = make_rsrc(p.xs + (size_t)m0 * G32, (uint32_t)(rows_m * G32));
+  S.K = K;
+  S.G32 = G32;
+  S.voff = (lane >> 2) * K + (((lane & 3) ^ (lane >> 4)) << 4);
+  S.soff = lane * G32;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // Prologue: half-steps 0..3 in flight; wait for half-step 0.
+  load_half<true>(S, smem, 0, nh, wave);
+  load_half<false>(S, smem, 1, nh, wave);
+  load_half<true>(S, smem, 2, nh, wave);
+  load_half<false>(S, smem, 3, nh, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<26>();  // half-step 0 (10 loads) landed; 8 + 10 + 8 may fly
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Frags F0, F1;
+  {
+    const FragAddr A = frag_addr(smem, 0, wn, wm, lane);
+    static_for<0, 24>([&](auto I) { read_piece<decltype(I)::value>(F0, A); });
+  }
+  for (int j = 0; j < nh; j += 2) {
+    half_step<true>(acc, F0, F1, S, smem, j, nh, wave, wn, wm, lane);
+    half_step<false>(acc, F1, F0, S, smem, j + 1, nh, wave, wn, wm, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  store_tile<EPI>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
+}
+
+template <int EPI>
+hipError_t launch(const Params& p, int nwg, hipStream_t st) {
+  static bool configured = false;  // per instantiation; benign race (idempotent)
+  auto kern = linear_prequant_ring<EPI>;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT), LDS, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace ring
 
 template <int EPI>
 hipError_t launch(const Params& p, int nwg, hipStream_t st) {
@@ -728,7 +964,8 @@ hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
   p.tiles_n = (int)((N + BN - 1) / BN);
   const int nwg = p.tiles_m * p.tiles_n;
   const bool ktail = (K % BK) != 0;
-  if (xs != nullptr && !ktail) return epi == 1 ? v2::launch<1>(p, nwg, stream) : v2::launch<0>(p, nwg, stream);
+  if (xs != nullptr && !ktail)
+    return epi == 1 ? v2::ring::launch<1>(p, nwg, stream) : v2::ring::launch<0>(p, nwg, stream);
   return xs == nullptr ? dispatch_epi<true>(p, ktail, epi, nwg, stream)
                        : dispatch_epi<false>(p, ktail, epi, nwg, stream);
 }
