@@ -1,25 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP8 W8A8 linear on one MI355X.
 
-One step = one call of the hot path on the fused self-attention q|k|v
-projection of Wan2.2-A14B over the full video latent: M = 75348 tokens,
-K = 5120, N = 15360, bf16 activations quantized to MXFP8 inside the GEMM,
-E4M3 weights with E8M0 scales (quantized once, before timing), f16 bias,
-bf16 output. Throughput counts the algorithmic 2*M*N*K FLOP.
+Workload: the fused self-attention q|k|v projection of Wan2.2-A14B over the
+full video latent of the official example (832x1104, 81 frames): M = 75348
+tokens, K = 5120, N = 15360. Activations bf16 (seeded synthetic, 0.1%
+outliers), weights E4M3 + E8M0 (quantized once before timing, as stored
+weights are), f16 bias, bf16 output.
 
-Prints ONE JSON line. Besides the contract fields it carries:
-  roofline      the dominant kernel (the fused linear) against the dense
-                MXFP8 MFMA peak, timed per launch with HIP events on the
-                launch stream; `traffic` comes from the committed rocprofv3
-                counter summary when it was taken on the current kernel
-                sources, else null;
+One step = the whole hot path on one batch: dynamic MX quantization of the
+activations (mx_quantize_act) followed by the block-scaled GEMM with bias
+(mx_linear_q). Throughput counts the algorithmic 2*M*N*K FLOP per step.
+
+Prints ONE JSON line. Besides the contract fields it carries
+  roofline      the dominant kernel (the GEMM) against the dense MXFP8 MFMA
+                peak, from its per-launch HIP-event times on the launch
+                stream; `traffic` is the HBM bytes per launch from the
+                committed rocprofv3 counter summary when that was taken on
+                the current kernel sources, else null;
   cpu_baseline  the float64 CPU oracle timed on a bounded row sample of the
                 same inputs;
-  extra         the quantize-then-GEMM path (mx_quantize_act + mx_linear_q)
-                and the quantizers' bandwidth.
+  extra         the activation quantizer's bandwidth, the fused-prologue
+                path (mx_linear), and the weight quantizer.
 
---profile-copy runs only a device copy of known size (for calibrating the
-HBM byte counters) and --no-cpu-baseline skips the oracle leg.
+Modes for profiling: --profile step|fused runs only those kernels (steps
+times, no oracle); --profile-copy runs a 1 GiB device copy used to calibrate
+the HBM byte counters.
 """
 
 import argparse
@@ -36,14 +41,14 @@ METRIC = "MXFP8 W8A8 linear TFLOP/s incl. act-quant, M=75348 K=5120; % of MXFP8 
 WORKLOAD = "qkv_75348x5120x15360"
 PEAK_MXFP8_TFLOPS = 5000.0  # MI355X dense MXFP8/FP8 MFMA peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_fused_qkv_75348x5120x15360.json")
-KERNEL_SOURCES = ["mx_gemm.hip", "mx_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_qkv_75348x5120x15360.json")
+GEMM_SOURCES = ["mx_gemm.hip", "mx_device.h"]
 CPU_SAMPLE_ROWS = 8192
 
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in GEMM_SOURCES:
         with open(os.path.join(ROOT, "mxfp8_w8a8_quantized_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -56,28 +61,38 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile", choices=["step", "fused"], help="run only these kernels")
     ap.add_argument("--profile-copy", action="store_true", help="run only a 1 GiB device copy")
     return ap.parse_args()
 
 
-def timed(torch, fn, steps, warmup):
-    """Runs fn warmup times, then steps times; returns (total ms, per-launch ms list)."""
+def timed_step(torch, fns, steps, warmup):
+    """Runs the kernels fns[0], fns[1], ... as one step, warmup times then
+    steps times, with a HIP event pair around each kernel on the current
+    stream. Returns (total ms, [per-kernel list of per-launch ms])."""
     for _ in range(warmup):
-        fn()
+        for f in fns:
+            f()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     start.record(stream)
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end), [a.elapsed_time(b) for a, b in evs]
+    per = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(len(fns))]
+    return start.elapsed_time(end), per
+
+
+def mean(v):
+    return sum(v) / len(v)
 
 
 def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
@@ -98,7 +113,7 @@ def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
     N = w_cpu.shape[0]
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
-        "value": 2.0 * rows * K * N / dt / 1e12,
+        "value": round(2.0 * rows * K * N / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
@@ -112,7 +127,7 @@ def main():
     if args.gpus != 1:
         print(
             f"bench.py measures one GPU only (got --gpus {args.gpus}); the linear shards over tokens with no "
-            "exchange, so multi-GPU throughput is N times the one-GPU figure by construction and is not measured.",
+            "exchange, so several GPUs are not measured here.",
             file=sys.stderr,
         )
         sys.exit(2)
@@ -150,20 +165,30 @@ def main():
     bias = b_cpu.to(dev)
     wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
     ws = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-    # Weight quantization happens once, outside the step (weights are stored
-    # quantized); timed here only for the quantizer's bandwidth.
-    _, wq_ms = timed(torch, lambda: mx.mx_quantize_weight(w, wq, ws), 3, 1)
+    # Weights are stored quantized: quantize once, outside the step.
+    _, wq_per = timed_step(torch, [lambda: mx.mx_quantize_weight(w, wq, ws)], 3, 1)
     del w
 
-    step = lambda: mx.mx_linear(x, wq, ws, bias, y=y)  # noqa: E731
-    total_ms, launch_ms = timed(torch, step, args.steps, args.warmup)
+    quant = lambda: mx.mx_quantize_act(x, xq, xs)  # noqa: E731
+    gemm = lambda: mx.mx_linear_q(xq, xs, wq, ws, bias, y=y)  # noqa: E731
+    fused = lambda: mx.mx_linear(x, wq, ws, bias, y=y)  # noqa: E731
+
+    if args.profile:
+        fns = [quant, gemm] if args.profile == "step" else [fused]
+        timed_step(torch, fns, args.steps, args.warmup)
+        print(json.dumps({"profiled": args.profile, "steps": args.steps}), flush=True)
+        return
+
+    total_ms, (q_ms, g_ms) = timed_step(torch, [quant, gemm], args.steps, args.warmup)
     flop = 2.0 * M * N * K
     ms_per_step = total_ms / args.steps
     value = flop / (ms_per_step * 1e-3) / 1e12
-    avg_launch = sum(launch_ms) / len(launch_ms)
-    achieved = flop / (avg_launch * 1e-3) / 1e12
+    gemm_ms = mean(g_ms)
+    achieved = flop / (gemm_ms * 1e-3) / 1e12
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -190,8 +215,7 @@ def main():
             "M": M,
             "K": K,
             "N": N,
-            "act_quant": "fused in GEMM prologue",
-            "epilogue": "f16 bias, bf16 out",
+            "step": "mx_quantize_act + mx_linear_q (bias, bf16 out)",
             "pct_of_mxfp8_peak": round(100.0 * value / PEAK_MXFP8_TFLOPS, 2),
         },
         "roofline": {
@@ -201,34 +225,32 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MXFP8_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "linear_kernel<fused>",
-            "launch_ms": round(avg_launch, 4),
+            "kernel": "linear_prequant_pp (block-scaled GEMM)",
+            "launch_ms": round(gemm_ms, 4),
+            "kernel_source_hash": kernel_source_hash(),
         },
     }
 
     if not args.no_extra:
-        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-        xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
-        _, q_ms = timed(torch, lambda: mx.mx_quantize_act(x, xq, xs), 10, 2)
-        _, l_ms = timed(torch, lambda: mx.mx_linear_q(xq, xs, wq, ws, bias, y=y), 10, 2)
-        qa = sum(q_ms) / len(q_ms)
-        lq = sum(l_ms) / len(l_ms)
+        qa = mean(q_ms)
         act_bytes = M * K * (2 + 1 + 1 / 32)
         w_bytes = N * K * (4 + 1 + 1 / 32)
-        wqa = sum(wq_ms) / len(wq_ms)
+        wqa = mean(wq_per[0])
+        _, (f_ms,) = timed_step(torch, [fused], 10, 2)
+        fa = mean(f_ms)
         out["extra"] = {
             "quantize_act_ms": round(qa, 4),
             "quantize_act_GBps": round(act_bytes / (qa * 1e-3) / 1e9, 1),
             "quantize_act_hbm_frac": round(act_bytes / (qa * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "linear_prequant_ms": round(lq, 4),
-            "two_pass_TFLOPs": round(flop / ((qa + lq) * 1e-3) / 1e12, 2),
+            "gemm_ms": round(gemm_ms, 4),
+            "fused_prologue_ms": round(fa, 4),
+            "fused_prologue_TFLOPs": round(flop / (fa * 1e-3) / 1e12, 2),
             "quantize_weight_f32_ms": round(wqa, 4),
             "quantize_weight_GBps": round(w_bytes / (wqa * 1e-3) / 1e9, 1),
         }
-        del xq, xs
 
     if not args.no_cpu_baseline:
-        del x, y
+        del x, y, xq, xs
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, b_cpu, CPU_SAMPLE_ROWS)
 
     print(json.dumps(out), flush=True)
