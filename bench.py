@@ -8,8 +8,10 @@ outliers), weights E4M3 + E8M0 (quantized once before timing, as stored
 weights are), f16 bias, bf16 output.
 
 One step = the whole hot path on one batch: dynamic MX quantization of the
-activations (mx_quantize_act) followed by the block-scaled GEMM with bias
-(mx_linear_q). Throughput counts the algorithmic 2*M*N*K FLOP per step.
+activations straight into the GEMM's slab layout (mx_quantize_act_slab)
+followed by the block-scaled GEMM with bias (mx_linear_slab). The weights are
+stored quantized in the slab layout (mx_quantize_weight_slab, once, before
+timing). Throughput counts the algorithmic 2*M*N*K FLOP per step.
 
 Prints ONE JSON line. Besides the contract fields it carries
   roofline      the dominant kernel (the GEMM) against the dense MXFP8 MFMA
@@ -19,12 +21,13 @@ Prints ONE JSON line. Besides the contract fields it carries
                 the current kernel sources, else null;
   cpu_baseline  the float64 CPU oracle timed on a bounded row sample of the
                 same inputs;
-  extra         the activation quantizer's bandwidth, the fused-prologue
-                path (mx_linear), and the weight quantizer.
+  extra         the activation quantizer's bandwidth, the same step on
+                row-major operands (mx_quantize_act + mx_linear_q), the
+                fused-prologue path (mx_linear), and the weight quantizer.
 
-Modes for profiling: --profile step|fused runs only those kernels (steps
-times, no oracle); --profile-copy runs a 1 GiB device copy used to calibrate
-the HBM byte counters.
+Modes for profiling: --profile step|rowmajor|fused runs only those kernels
+(steps times, no oracle); --profile-copy runs a 1 GiB device copy used to
+calibrate the HBM byte counters.
 """
 
 import argparse
@@ -61,7 +64,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--profile", choices=["step", "fused"], help="run only these kernels")
+    ap.add_argument("--profile", choices=["step", "rowmajor", "fused"], help="run only these kernels")
     ap.add_argument("--profile-copy", action="store_true", help="run only a 1 GiB device copy")
     return ap.parse_args()
 
@@ -163,22 +166,26 @@ def main():
     x = x_cpu.to(dev)
     w = w_cpu.to(dev)
     bias = b_cpu.to(dev)
-    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    ws = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
-    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     # Weights are stored quantized: quantize once, outside the step.
-    _, wq_per = timed_step(torch, [lambda: mx.mx_quantize_weight(w, wq, ws)], 3, 1)
+    wsl = mx.mx_quantize_weight_slab(w)
+    _, wq_per = timed_step(torch, [lambda: mx.mx_quantize_weight_slab(w, wsl)], 3, 1)
+    xsl = mx.mx_quantize_act_slab(x)
+
+    quant = lambda: mx.mx_quantize_act_slab(x, xsl)  # noqa: E731
+    gemm = lambda: mx.mx_linear_slab(xsl, wsl, bias, y=y)  # noqa: E731
+
+    rowmajor = None
+    if args.profile in ("rowmajor", "fused") or (not args.profile and not args.no_extra):
+        wq, ws = mx.mx_quantize_weight(w)
+        xq, xs = mx.mx_quantize_act(x)
+        rowmajor = [lambda: mx.mx_quantize_act(x, xq, xs), lambda: mx.mx_linear_q(xq, xs, wq, ws, bias, y=y)]
+        fused = lambda: mx.mx_linear(x, wq, ws, bias, y=y)  # noqa: E731
     del w
 
-    quant = lambda: mx.mx_quantize_act(x, xq, xs)  # noqa: E731
-    gemm = lambda: mx.mx_linear_q(xq, xs, wq, ws, bias, y=y)  # noqa: E731
-    fused = lambda: mx.mx_linear(x, wq, ws, bias, y=y)  # noqa: E731
-
     if args.profile:
-        fns = [quant, gemm] if args.profile == "step" else [fused]
+        fns = {"step": [quant, gemm], "rowmajor": rowmajor, "fused": [fused] if rowmajor else None}[args.profile]
         timed_step(torch, fns, args.steps, args.warmup)
         print(json.dumps({"profiled": args.profile, "steps": args.steps}), flush=True)
         return
@@ -215,7 +222,7 @@ def main():
             "M": M,
             "K": K,
             "N": N,
-            "step": "mx_quantize_act + mx_linear_q (bias, bf16 out)",
+            "step": "mx_quantize_act_slab + mx_linear_slab (bias, bf16 out)",
             "pct_of_mxfp8_peak": round(100.0 * value / PEAK_MXFP8_TFLOPS, 2),
         },
         "roofline": {
@@ -225,7 +232,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MXFP8_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "linear_prequant_pp (block-scaled GEMM)",
+            "kernel": "linear_slab_kernel (block-scaled GEMM)",
             "launch_ms": round(gemm_ms, 4),
             "kernel_source_hash": kernel_source_hash(),
         },
@@ -236,6 +243,7 @@ def main():
         act_bytes = M * K * (2 + 1 + 1 / 32)
         w_bytes = N * K * (4 + 1 + 1 / 32)
         wqa = mean(wq_per[0])
+        rm_total, (rq_ms, rg_ms) = timed_step(torch, rowmajor, 10, 2)
         _, (f_ms,) = timed_step(torch, [fused], 10, 2)
         fa = mean(f_ms)
         out["extra"] = {
@@ -243,6 +251,9 @@ def main():
             "quantize_act_GBps": round(act_bytes / (qa * 1e-3) / 1e9, 1),
             "quantize_act_hbm_frac": round(act_bytes / (qa * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "gemm_ms": round(gemm_ms, 4),
+            "rowmajor_step_ms": round(rm_total / 10, 4),
+            "rowmajor_step_TFLOPs": round(flop / (rm_total / 10 * 1e-3) / 1e12, 2),
+            "rowmajor_gemm_ms": round(mean(rg_ms), 4),
             "fused_prologue_ms": round(fa, 4),
             "fused_prologue_TFLOPs": round(flop / (fa * 1e-3) / 1e12, 2),
             "quantize_weight_f32_ms": round(wqa, 4),
@@ -250,7 +261,7 @@ def main():
         }
 
     if not args.no_cpu_baseline:
-        del x, y, xq, xs
+        del x, y, xsl, rowmajor
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, b_cpu, CPU_SAMPLE_ROWS)
 
     print(json.dumps(out), flush=True)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 1
+#define MX_ABI_VERSION 2
 
 typedef enum {
   MX_OK = 0,
@@ -111,6 +111,46 @@ int mx_linear(const void* x, int64_t M, int64_t K,
 int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                 const uint8_t* wq, const uint8_t* ws, int64_t N,
                 const void* bias, int epilogue, void* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Slab layout. The same codes and scales, stored for the GEMM's tiles rather
+ * than by row: with R = mx_slab_rows(rows) (rows rounded up to 256) and K a
+ * multiple of 64,
+ *   codes   q  uint8 [K/64][R][64]   q[j][r][i] = code of row r, k = 64 j + i
+ *   scales  s  uint8 [K/64][R][2]    s[j][r][h] = scale of row r, group 2 j + h
+ * Rows rows..R-1 hold zero codes and zero scales. One 256-row tile's share of
+ * a 64-K slab is then one contiguous run (16 KB of codes, 512 B of scales),
+ * which the GEMM streams with whole-line loads. Values are bit-identical to
+ * the row-major calls above; only the placement differs.
+ * ------------------------------------------------------------------------ */
+
+/* R for a slab-layout operand of `rows` rows; -1 if rows < 0. */
+int64_t mx_slab_rows(int64_t rows);
+
+/* mx_quantize_act writing the slab layout. K % 64 == 0; q: uint8
+ * [K/64][R][64], s: uint8 [K/64][R][2] with R = mx_slab_rows(M). */
+int mx_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx,
+                         uint8_t* q, uint8_t* s, void* stream);
+
+/* mx_quantize_weight writing the slab layout (R = mx_slab_rows(N)). */
+int mx_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
+                            uint8_t* q, uint8_t* s, void* stream);
+
+/* Row-major codes q [rows][K] and scales s [rows][K/32] (e.g. weights that
+ * were stored quantized) to the slab layout qslab, sslab. K % 64 == 0; codes
+ * 16-byte aligned, scales 2-byte aligned; outputs must not overlap inputs. */
+int mx_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
+                 uint8_t* qslab, uint8_t* sslab, void* stream);
+
+/* The linear of mx_linear_q on slab-layout operands: xq [K/64][RM][64],
+ * xs [K/64][RM][2] (RM = mx_slab_rows(M)), wq [K/64][RN][64], ws [K/64][RN][2]
+ * (RN = mx_slab_rows(N)); bias f16 [N] or NULL; y bf16 [M][N] row-major.
+ * K % 64 == 0 (else MX_ERR_INVALID_ARGUMENT), N % 16 == 0 (else
+ * MX_ERR_UNSUPPORTED); codes and y 16-byte aligned, scales 4-byte aligned.
+ * The result is bit-identical to mx_linear_q on the same codes and scales. */
+int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                   const uint8_t* wq, const uint8_t* ws, int64_t N,
+                   const void* bias, int epilogue, void* y, void* stream);
 
 #ifdef __cplusplus
 }

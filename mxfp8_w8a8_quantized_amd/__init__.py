@@ -8,6 +8,7 @@ If the built library ``libmxfp8.so`` is missing, every call raises.
 
 import ctypes
 import os
+from typing import NamedTuple
 
 import torch
 
@@ -36,6 +37,11 @@ SIGNATURES = {
     "mx_quantize_weight": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_linear": ([_P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_linear_q": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
+    "mx_slab_rows": ([_I64], _I64),
+    "mx_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
+    "mx_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
+    "mx_slab_pack": ([_P, _P, _I64, _I64, _P, _P, _P], _INT),
+    "mx_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
 }
 
 
@@ -184,5 +190,116 @@ def mx_linear_q(xq, xs, wq, ws, bias=None, gelu=False, y=None):
     with torch.cuda.device(dev):
         _check(
             lib().mx_linear_q(_ptr(xq), _ptr(xs), M, K, _ptr(wq), _ptr(ws), N, _ptr(bias), epi, _ptr(y), _stream(dev))
+        )
+    return y
+
+
+class Slab(NamedTuple):
+    """An operand in the slab layout: codes q uint8 [K/64, R, 64], scales s
+    uint8 [K/64, R, 2], R = mx_slab_rows(rows); rows past `rows` are zero."""
+
+    q: torch.Tensor
+    s: torch.Tensor
+    rows: int
+
+    @property
+    def K(self):
+        return self.q.shape[0] * 64
+
+
+def mx_slab_rows(rows):
+    return lib().mx_slab_rows(rows)
+
+
+def _slab_out(rows, K, dev, out):
+    R = mx_slab_rows(rows)
+    if out is None:
+        return Slab(
+            torch.empty((K // 64, R, 64), dtype=torch.uint8, device=dev),
+            torch.empty((K // 64, R, 2), dtype=torch.uint8, device=dev),
+            rows,
+        )
+    _need(out.q, "out.q", torch.uint8, dev)
+    _need(out.s, "out.s", torch.uint8, dev)
+    if out.q.shape != (K // 64, R, 64) or out.s.shape != (K // 64, R, 2) or out.rows != rows:
+        raise ValueError(f"out must hold [{K // 64}, {R}, 64] codes and [{K // 64}, {R}, 2] scales for {rows} rows")
+    return out
+
+
+def mx_quantize_act_slab(x, out=None):
+    """bf16 [M, K] (rows may be strided, K % 64 == 0) -> Slab of its MX codes and scales."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    if K % 64 != 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    dev = x.device
+    out = _slab_out(M, K, dev, out)
+    ld = x.stride(0) if M > 1 else K
+    with torch.cuda.device(dev):
+        _check(lib().mx_quantize_act_slab(_ptr(x), M, K, ld, _ptr(out.q), _ptr(out.s), _stream(dev)))
+    return out
+
+
+def mx_quantize_weight_slab(w, out=None):
+    """fp32 or bf16 [N, K] (K % 64 == 0) -> Slab of its MX codes and scales."""
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be 2-D with unit column stride")
+    dt = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}.get(w.dtype)
+    if dt is None:
+        raise TypeError(f"w must be float32 or bfloat16, got {w.dtype}")
+    N, K = w.shape
+    if K % 64 != 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    dev = w.device
+    out = _slab_out(N, K, dev, out)
+    ld = w.stride(0) if N > 1 else K
+    with torch.cuda.device(dev):
+        _check(lib().mx_quantize_weight_slab(_ptr(w), dt, N, K, ld, _ptr(out.q), _ptr(out.s), _stream(dev)))
+    return out
+
+
+def mx_slab_pack(q, s, out=None):
+    """Row-major codes uint8 [rows, K] and scales uint8 [rows, K/32] -> Slab."""
+    dev = q.device
+    _need(q, "q", torch.uint8, dev)
+    _need(s, "s", torch.uint8, dev)
+    rows, K = q.shape
+    if s.shape != (rows, K // 32):
+        raise ValueError("s must be [rows, K/32]")
+    if K % 64 != 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    out = _slab_out(rows, K, dev, out)
+    with torch.cuda.device(dev):
+        _check(lib().mx_slab_pack(_ptr(q), _ptr(s), rows, K, _ptr(out.q), _ptr(out.s), _stream(dev)))
+    return out
+
+
+def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
+    """y = bf16(epi(xhat @ what^T + bias)) on slab operands x (tokens) and w (weights)."""
+    dev = x.q.device
+    for name, t in (("x.q", x.q), ("x.s", x.s), ("w.q", w.q), ("w.s", w.s)):
+        _need(t, name, torch.uint8, dev)
+    M, N, K = x.rows, w.rows, x.K
+    if w.K != K:
+        raise ValueError(f"x has K = {K}, w has K = {w.K}")
+    for name, sl in (("x", x), ("w", w)):
+        R = mx_slab_rows(sl.rows)
+        if sl.q.shape != (K // 64, R, 64) or sl.s.shape != (K // 64, R, 2):
+            raise ValueError(f"{name} is not a slab of {sl.rows} rows and K = {K}")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be f16 [N]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_slab(
+                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _stream(dev)
+            )
         )
     return y

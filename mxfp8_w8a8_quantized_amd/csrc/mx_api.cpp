@@ -104,6 +104,29 @@ int check_linear_common(int64_t M, int64_t K, const uint8_t* wq, const uint8_t* 
   return MX_OK;
 }
 
+// Quantizer arguments: x [rows][ld] of dtype dt; outputs row-major or slab.
+int check_quantize(const void* x, int dt, int64_t rows, int64_t K, int64_t ld, const uint8_t* q, const uint8_t* s,
+                   bool slab) {
+  int st;
+  if (dt != MX_DT_BF16 && dt != MX_DT_F32) return fail(MX_ERR_INVALID_ARGUMENT, "unknown weight dtype %d", dt);
+  if ((st = check_rows("rows", rows)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (slab && K % 64 != 0)
+    return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
+  const int64_t es = dt == MX_DT_F32 ? 4 : 2;
+  if (ld < K || (ld * es) % 16 != 0)
+    return fail(MX_ERR_INVALID_ARGUMENT, "pitch %lld must be >= K with 16-byte aligned rows", (long long)ld);
+  if (rows == 0) return MX_OK;
+  if (x == nullptr || q == nullptr || s == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "input and codes must be 16-byte aligned");
+  const uint64_t R = slab ? (uint64_t)mx::slab_rows(rows) : (uint64_t)rows;
+  const uint64_t xbytes = ((uint64_t)(rows - 1) * ld + K) * es;
+  const uint64_t nq = R * K, ns = R * (K / 32);
+  if (overlap(q, nq, x, xbytes) || overlap(s, ns, x, xbytes) || overlap(q, nq, s, ns))
+    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
+  return check_device();
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,42 +148,59 @@ int mx_last_hip_error(void) { return t_last_hip; }
 const char* mx_last_error_message(void) { return t_msg; }
 
 int mx_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, uint8_t* s, void* stream) {
-  int st;
-  if ((st = check_rows("M", M)) != MX_OK) return st;
-  if ((st = check_k(K)) != MX_OK) return st;
-  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
-  if (M == 0) return MX_OK;
-  if (x == nullptr || q == nullptr || s == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (!aligned(x, 16) || !aligned(q, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "x and q must be 16-byte aligned");
-  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2;
-  if (overlap(q, (uint64_t)M * K, x, xbytes) || overlap(s, (uint64_t)M * (K / 32), x, xbytes) ||
-      overlap(q, (uint64_t)M * K, s, (uint64_t)M * (K / 32)))
-    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
-  if ((st = check_device()) != MX_OK) return st;
+  const int st = check_quantize(x, MX_DT_BF16, M, K, ldx, q, s, false);
+  if (st != MX_OK || M == 0) return st;
   (void)hipGetLastError();
   return finish(mx::launch_quantize(0, x, M, K, ldx, q, s, (hipStream_t)stream), "quantize launch");
 }
 
 int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q, uint8_t* s,
                        void* stream) {
-  int st;
-  if (wdtype != MX_DT_BF16 && wdtype != MX_DT_F32) return fail(MX_ERR_INVALID_ARGUMENT, "unknown weight dtype %d", wdtype);
-  if ((st = check_rows("N", N)) != MX_OK) return st;
-  if ((st = check_k(K)) != MX_OK) return st;
-  const int64_t es = wdtype == MX_DT_F32 ? 4 : 2;
-  if (ldw < K || (ldw * es) % 16 != 0)
-    return fail(MX_ERR_INVALID_ARGUMENT, "ldw = %lld must be >= K with 16-byte aligned rows", (long long)ldw);
-  if (N == 0) return MX_OK;
-  if (w == nullptr || q == nullptr || s == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (!aligned(w, 16) || !aligned(q, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "w and q must be 16-byte aligned");
-  const uint64_t wbytes = ((uint64_t)(N - 1) * ldw + K) * es;
-  if (overlap(q, (uint64_t)N * K, w, wbytes) || overlap(s, (uint64_t)N * (K / 32), w, wbytes) ||
-      overlap(q, (uint64_t)N * K, s, (uint64_t)N * (K / 32)))
-    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
-  if ((st = check_device()) != MX_OK) return st;
+  const int st = check_quantize(w, wdtype, N, K, ldw, q, s, false);
+  if (st != MX_OK || N == 0) return st;
   (void)hipGetLastError();
   return finish(mx::launch_quantize(wdtype == MX_DT_F32 ? 1 : 0, w, N, K, ldw, q, s, (hipStream_t)stream),
                 "quantize launch");
+}
+
+int64_t mx_slab_rows(int64_t rows) { return rows < 0 ? -1 : mx::slab_rows(rows); }
+
+int mx_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, uint8_t* s, void* stream) {
+  const int st = check_quantize(x, MX_DT_BF16, M, K, ldx, q, s, true);
+  if (st != MX_OK || M == 0) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_quantize_slab(0, x, M, K, ldx, q, s, (hipStream_t)stream), "quantize launch");
+}
+
+int mx_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q, uint8_t* s,
+                            void* stream) {
+  const int st = check_quantize(w, wdtype, N, K, ldw, q, s, true);
+  if (st != MX_OK || N == 0) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_quantize_slab(wdtype == MX_DT_F32 ? 1 : 0, w, N, K, ldw, q, s, (hipStream_t)stream),
+                "quantize launch");
+}
+
+int mx_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, uint8_t* qslab, uint8_t* sslab,
+                 void* stream) {
+  int st;
+  if ((st = check_rows("rows", rows)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (K % 64 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
+  if (rows == 0) return MX_OK;
+  if (q == nullptr || s == nullptr || qslab == nullptr || sslab == nullptr)
+    return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(q, 16) || !aligned(qslab, 16) || !aligned(s, 2) || !aligned(sslab, 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "codes must be 16-byte and scales 2-byte aligned");
+  const uint64_t R = (uint64_t)mx::slab_rows(rows);
+  const uint64_t nq = (uint64_t)rows * K, ns = (uint64_t)rows * (K / 32);
+  const uint64_t oq = R * K, os = R * (K / 32);
+  if (overlap(qslab, oq, q, nq) || overlap(qslab, oq, s, ns) || overlap(sslab, os, q, nq) ||
+      overlap(sslab, os, s, ns) || overlap(qslab, oq, sslab, os))
+    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_slab_pack(q, s, rows, K, qslab, sslab, (hipStream_t)stream), "slab pack launch");
 }
 
 int mx_linear(const void* x, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias,
@@ -187,6 +227,34 @@ int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, cons
   if ((st = check_device()) != MX_OK) return st;
   (void)hipGetLastError();
   return finish(mx::launch_linear(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream), "linear launch");
+}
+
+int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws,
+                   int64_t N, const void* bias, int epilogue, void* y, void* stream) {
+  int st;
+  if ((st = check_rows("M", M)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (K % 64 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
+  if (N < 0) return fail(MX_ERR_INVALID_ARGUMENT, "N = %lld is negative", (long long)N);
+  if (N > kMaxKN) return fail(MX_ERR_UNSUPPORTED, "N = %lld exceeds the supported 2^20", (long long)N);
+  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH)
+    return fail(MX_ERR_INVALID_ARGUMENT, "unknown epilogue %d", epilogue);
+  if (M == 0 || N == 0) return MX_OK;
+  if (N % 16 != 0) return fail(MX_ERR_UNSUPPORTED, "N = %lld must be a multiple of 16", (long long)N);
+  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr || y == nullptr)
+    return fail(MX_ERR_INVALID_ARGUMENT, "NULL operand or output pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4))
+    return fail(MX_ERR_INVALID_ARGUMENT, "codes and y must be 16-byte aligned, scales 4-byte aligned");
+  if (bias != nullptr && !aligned(bias, 2)) return fail(MX_ERR_INVALID_ARGUMENT, "bias must be 2-byte aligned");
+  const uint64_t RM = (uint64_t)mx::slab_rows(M), RN = (uint64_t)mx::slab_rows(N);
+  const uint64_t yb = (uint64_t)M * N * 2;
+  if (overlap(y, yb, xq, RM * K) || overlap(y, yb, xs, RM * (K / 32)) || overlap(y, yb, wq, RN * K) ||
+      overlap(y, yb, ws, RN * (K / 32)) || overlap(y, yb, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
+                "linear launch");
 }
 
 }  // extern "C"

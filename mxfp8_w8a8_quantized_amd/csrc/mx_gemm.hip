@@ -553,6 +553,195 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
 
 }  // namespace pp
 
+// ---------------------------------------------------------------------------
+// GEMM on the slab layout (see mx.h): operands as K-slabs of 64, codes
+// [K/64][R][64] and scales [K/64][R][2] with R the row count rounded up to
+// 256, so one tile's share of a slab is one contiguous run (16 KB of codes,
+// 512 B of scales) instead of 256 row pieces 5 KB apart. This halves the
+// cache-line requests per byte (the row-major scales alone cost as many line
+// lookups as all the codes) and lets the loads stream from whole lines.
+//
+// 8 waves and the same 128 (n) x 64 (m) wave sub-tiles and epilogue as the
+// pp kernel. K advances in half-steps of 64 through a ring of 4 LDS regions;
+// waves 0..3 issue the refill of half-step j+4 right after the barrier of
+// half-step j, so each load has three half-steps (about 3000 cycles at full
+// MFMA rate) to land, and about 100 KB per CU are in flight:
+//
+//   half-step j:  wait for this wave's loads of j+1, barrier;
+//                 (loader waves) issue the loads of j+4 into region j % 4;
+//                 8 MFMAs on the fragments of j (registers), with the LDS
+//                 reads of the fragments of j+1 (region (j+1) % 4).
+//
+// Region layout: weight codes 256 rows x 64 B, 16-byte chunk c of row r at
+// slot c ^ ((r >> 2) & 3) (conflict-free for 16-lane phases of b128 reads);
+// token codes the same; then the scales of both, [row][2] bytes. Loads past
+// the last half-step use an empty resource and write zeros that nobody reads.
+namespace slab {
+
+constexpr int NT8 = 512;
+constexpr int R_W = 0, R_X = 16384, R_WS = 32768, R_XS = 33280;
+constexpr int REGION = 33792;
+constexpr int LDS = 4 * REGION;
+constexpr int LOADS_PER_HALF = 9;  // per loader wave: 4 + 4 code DMAs, 1 scale DMA
+
+using pp::Frags;
+
+struct Src {
+  const uint8_t* w;  // tile origin in slab 0: codes, then scales
+  const uint8_t* x;
+  const uint8_t* ws;
+  const uint8_t* xs;
+  uint64_t w_slab, x_slab;  // bytes between consecutive code slabs
+  int nh;                   // half-steps (K / 64)
+  int voff;                 // lane part of a code DMA offset
+};
+
+// Loads of half-step j by loader wave `wave` (0..3): 16-row blocks 4 wave ..
+// 4 wave + 3 of both code operands (1 KB each; lane L takes row L/4, global
+// chunk (L%4) ^ (L/16) into LDS slot L%4) and one 256-byte half of the
+// weight (waves 0, 1) or token (waves 2, 3) scales.
+__device__ __forceinline__ void issue_half(const Src& S, uint8_t* smem, int j, int wave, int lane) {
+  uint8_t* reg = smem + (j & 3) * REGION;
+  const bool valid = j < S.nh;
+  const uint32_t nc = valid ? 16384u : 0u, ns = valid ? 512u : 0u;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(S.w + (uint64_t)j * S.w_slab, nc);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x + (uint64_t)j * S.x_slab, nc);
+  const bool wscale = wave < 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(wscale ? S.ws + (uint64_t)j * (S.w_slab >> 5) : S.xs + (uint64_t)j * (S.x_slab >> 5), ns);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(reg + (wscale ? R_WS : R_XS) + (wave & 1) * 256), 4,
+                                           lane * 4, (wave & 1) * 256, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = wave * 4 + u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(reg + R_W + q * 1024), 16, S.voff, q * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
+  }
+}
+
+// Fragments of a region for the 32x32x64 MFMA: lane l, fragment f reads row
+// base + 32 f + l%32, K bytes [16 (l/32), +16) and [32 + 16 (l/32), +16) of
+// the 64, and the scale of group l/32 of the half-step.
+__device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn, int wm, int lane) {
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int sw = (r32 >> 2) & 3;
+  const int c0 = (hi ^ sw) << 4, c1 = ((2 + hi) ^ sw) << 4;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int row = wn * 128 + 32 * f + r32;
+    const uint8_t* ra = reg + R_W + row * 64;
+    const i32x4 a0 = *(const i32x4*)(ra + c0), a1 = *(const i32x4*)(ra + c1);
+    F.a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    F.sa[f] = reg[R_WS + row * 2 + hi];
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int row = wm * 64 + 32 * f + r32;
+    const uint8_t* rb = reg + R_X + row * 64;
+    const i32x4 b0 = *(const i32x4*)(rb + c0), b1 = *(const i32x4*)(rb + c1);
+    F.b[f] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    F.sb[f] = reg[R_XS + row * 2 + hi];
+  }
+}
+
+// Half-step j: publish region (j+1) % 4, refill region j % 4 with half-step
+// j+4 (loader waves), MFMAs of j from `cur` while `nxt` is read from region
+// (j+1) % 4. The lgkmcnt(0) in the wait keeps any wave's refill from
+// overtaking another wave's last reads of the region being refilled.
+template <bool LOADER>
+__device__ __forceinline__ void half_step(f32x16 (&acc)[4][2], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
+                                          int j, int wave, int wn, int wm, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS_PER_HALF) : "memory");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LOADER) issue_half(S, smem, j + 4, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(nxt, smem + ((j + 1) & 3) * REGION, wn, wm, lane);
+  pp::mma8(acc, cur);
+}
+
+// The K loop, one copy for loader and one for compute-only waves, so that no
+// branch splits a half-step (a split lets the compiler sink the MFMAs of one
+// half-step past the next barrier). Both copies pass the same barriers.
+template <bool LOADER>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[4][2], Frags& F0, Frags& F1, const Src& S, uint8_t* smem,
+                                       int wave, int wn, int wm, int lane) {
+  const int nh = S.nh;
+  int j = 0;
+  for (; j + 1 < nh; j += 2) {
+    half_step<LOADER>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+    half_step<LOADER>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
+  }
+  if (j < nh) half_step<LOADER>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT8, 1) void linear_slab_kernel(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_m = min(p.M - m0, BM);
+  const int rows_n = min(p.N - n0, BN);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const bool loader = wave < 4;
+
+  Src S;
+  S.w_slab = (uint64_t)p.tiles_n * BN * 64;
+  S.x_slab = (uint64_t)p.tiles_m * BM * 64;
+  S.w = p.wq + (size_t)n0 * 64;
+  S.x = p.x + (size_t)m0 * 64;
+  S.ws = p.ws + (size_t)n0 * 2;
+  S.xs = p.xs + (size_t)m0 * 2;
+  S.nh = p.K >> 6;
+  S.voff = (lane >> 2) * 64 + (((lane & 3) ^ (lane >> 4)) << 4);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  if (loader) {
+    issue_half(S, smem, 0, wave, lane);
+    issue_half(S, smem, 1, wave, lane);
+    issue_half(S, smem, 2, wave, lane);
+    issue_half(S, smem, 3, wave, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * LOADS_PER_HALF) : "memory");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Frags F0, F1;
+  read_frags(F0, smem, wn, wm, lane);
+  if (loader)
+    k_loop<true>(acc, F0, F1, S, smem, wave, wn, wm, lane);
+  else
+    k_loop<false>(acc, F0, F1, S, smem, wave, wn, wm, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  pp::store_tile8<EPI>(acc, p, smem + wave * 16384, m0, n0, rows_m, rows_n, wn, wm, lane);
+}
+
+template <int EPI>
+hipError_t launch(const Params& p, int nwg, hipStream_t st) {
+  static bool configured = false;  // per instantiation; benign race (idempotent)
+  auto kern = linear_slab_kernel<EPI>;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT8), LDS, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace slab
+
 template <bool FUSED, bool KTAIL, int EPI>
 hipError_t launch_variant(const Params& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
@@ -596,6 +785,24 @@ hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
     return epi == 1 ? pp::launch<1>(p, nwg, stream) : pp::launch<0>(p, nwg, stream);
   return xs == nullptr ? dispatch_epi<true>(p, ktail, epi, nwg, stream)
                        : dispatch_epi<false>(p, ktail, epi, nwg, stream);
+}
+
+hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                              const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, hipStream_t stream) {
+  Params p;
+  p.x = xq;
+  p.xs = xs;
+  p.wq = wq;
+  p.ws = ws;
+  p.bias = (const uint16_t*)bias;
+  p.y = (uint16_t*)y;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const int nwg = p.tiles_m * p.tiles_n;
+  return epi == 1 ? slab::launch<1>(p, nwg, stream) : slab::launch<0>(p, nwg, stream);
 }
 
 }  // namespace mx

@@ -12,11 +12,29 @@ namespace mx {
 hipError_t launch_quantize(int kind, const void* x, int64_t rows, int64_t K, int64_t ld,
                            uint8_t* q, uint8_t* s, hipStream_t stream);
 
+// Rows of a slab-layout operand: `rows` rounded up to the 256-row tile.
+inline int64_t slab_rows(int64_t rows) { return (rows + 255) / 256 * 256; }
+
+// The same quantization written in the slab layout (codes [K/64][R][64],
+// scales [K/64][R][2], R = slab_rows(rows); pad rows are zero). K % 64 == 0.
+hipError_t launch_quantize_slab(int kind, const void* x, int64_t rows, int64_t K, int64_t ld,
+                                uint8_t* q, uint8_t* s, hipStream_t stream);
+
+// Row-major codes [rows][K] and scales [rows][K/32] to the slab layout.
+hipError_t launch_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
+                            uint8_t* qo, uint8_t* so, hipStream_t stream);
+
 // The block-scaled GEMM. When xs == nullptr, x is bf16 [M][K] and is
 // quantized in the prologue; otherwise x holds E4M3 codes [M][K] and xs the
 // E8M0 scales [M][K/32]. epi: 0 none, 1 GELU-tanh.
 hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
                          const uint8_t* wq, const uint8_t* ws, int64_t N,
                          const void* bias, int epi, void* y, hipStream_t stream);
+
+// The block-scaled GEMM on operands in the slab layout (mx.h): codes
+// [K/64][R][64], scales [K/64][R][2], R = rows rounded up to 256; K % 64 == 0.
+hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                              const uint8_t* wq, const uint8_t* ws, int64_t N,
+                              const void* bias, int epi, void* y, hipStream_t stream);
 
 }  // namespace mx

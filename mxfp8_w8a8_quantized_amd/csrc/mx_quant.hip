@@ -4,9 +4,15 @@
 // activations, E4M3 weights with per-32 E8M0 scales).
 //
 // HBM-bound: each lane owns 8 consecutive elements (a quarter of a group of
-// 32), so a wave streams 512 contiguous elements per item with 16- or 32-byte
-// loads and 8-byte code stores; the group maximum is reduced across the four
-// lanes of a DPP quad. Every thread keeps 4 items in flight.
+// 32), loaded with 16- or 32-byte loads and stored as 8 code bytes; the group
+// maximum is reduced across the four lanes of a DPP quad. Every thread keeps
+// 4 items in flight.
+//
+// Row-major output: a wave streams 512 contiguous elements of one row.
+// Slab output (codes [K/64][R][64], scales [K/64][R][2], R = rows rounded up
+// to 256): 16 consecutive lanes cover two rows x 64 K, so each group of 16
+// lanes stores one whole 128-byte line of a slab; rows rows..R-1 are written
+// as zero codes and zero scales.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -16,29 +22,43 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kItems = 4;  // items (8-element quarters) in flight per thread
 
-template <bool F32, typename Idx>
+template <bool F32, bool SLAB, typename Idx>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restrict__ x, Idx rows, Idx K, Idx ld,
-                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+                                                            Idx R, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const Idx qpr = K / 8;  // quarters per row; a multiple of 4
-  const Idx total = rows * qpr;
+  const Idx total = (SLAB ? R : rows) * qpr;
   const Idx stride = (Idx)gridDim.x * kThreads;
   const Idx gpr = K / 32;
+  const Idx nslab = K / 64;
   for (Idx base = (Idx)blockIdx.x * kThreads + threadIdx.x; base < total; base += stride * kItems) {
-    // All four lanes of a quad see the same validity: total and stride are
-    // multiples of 4 and quads are 4-aligned.
+    // All four lanes of a quad see the same validity and row: total and
+    // stride are multiples of 4 (of 16 in slab order) and quads are 4-aligned.
     uint32_t raw[kItems][8];
-    Idx row[kItems], cq[kItems];
-    bool ok[kItems];
+    Idx row[kItems], cq[kItems], qoff[kItems], soff[kItems];
+    bool ok[kItems], in[kItems];
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
       const Idx u = base + (Idx)j * stride;
       ok[j] = u < total;
-      row[j] = ok[j] ? u / qpr : 0;
-      cq[j] = ok[j] ? u - row[j] * qpr : 0;
+      if (SLAB) {
+        const Idx t = ok[j] ? (u & 15) : 0, rest = ok[j] ? (u >> 4) : 0;
+        const Idx sl = rest % nslab, pair = rest / nslab;
+        row[j] = 2 * pair + (t >> 3);
+        cq[j] = sl * 8 + (t & 7);
+        qoff[j] = sl * R * 64 + row[j] * 64 + (t & 7) * 8;
+        soff[j] = sl * R * 2 + row[j] * 2 + ((t & 7) >> 2);
+        in[j] = ok[j] && row[j] < rows;
+      } else {
+        row[j] = ok[j] ? u / qpr : 0;
+        cq[j] = ok[j] ? u - row[j] * qpr : 0;
+        qoff[j] = row[j] * K + cq[j] * 8;
+        soff[j] = row[j] * gpr + (cq[j] >> 2);
+        in[j] = ok[j];
+      }
       if (F32) {
         const float* p = (const float*)x + (size_t)row[j] * (size_t)ld + (size_t)cq[j] * 8;
-        i32x4 a = ok[j] ? *(const i32x4*)p : i32x4{0, 0, 0, 0};
-        i32x4 b = ok[j] ? *(const i32x4*)(p + 4) : i32x4{0, 0, 0, 0};
+        i32x4 a = in[j] ? *(const i32x4*)p : i32x4{0, 0, 0, 0};
+        i32x4 b = in[j] ? *(const i32x4*)(p + 4) : i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           raw[j][t] = (uint32_t)a[t];
@@ -46,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restri
         }
       } else {
         const uint16_t* p = (const uint16_t*)x + (size_t)row[j] * (size_t)ld + (size_t)cq[j] * 8;
-        i32x4 a = ok[j] ? *(const i32x4*)p : i32x4{0, 0, 0, 0};
+        i32x4 a = in[j] ? *(const i32x4*)p : i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 4; ++t) raw[j][t] = (uint32_t)a[t];
       }
@@ -63,24 +83,54 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restri
       } else {
         quantize8_bf16(raw[j], codes, sc);
       }
-      *(i32x2*)(q + (size_t)row[j] * (size_t)K + (size_t)cq[j] * 8) = i32x2{(int)codes[0], (int)codes[1]};
-      if ((cq[j] & 3) == 0) s[(size_t)row[j] * (size_t)gpr + (size_t)(cq[j] >> 2)] = (uint8_t)sc;
+      *(i32x2*)(q + (size_t)qoff[j]) = i32x2{(int)codes[0], (int)codes[1]};
+      if ((cq[j] & 3) == 0) s[(size_t)soff[j]] = (uint8_t)sc;
     }
   }
 }
 
-template <bool F32>
-hipError_t launch_typed(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s, hipStream_t st) {
-  const int64_t total = rows * (K / 8);
-  int64_t blocks = (total + (int64_t)kThreads * kItems - 1) / ((int64_t)kThreads * kItems);
+// Row-major codes [rows][K] and scales [rows][K/32] to the slab layout: one
+// 16-byte piece per thread, 8 consecutive threads per 128-byte slab line
+// (two rows x 64 B); rows rows..R-1 become zeros.
+template <typename Idx>
+__global__ __launch_bounds__(kThreads) void slab_pack_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                             Idx rows, Idx K, Idx R, uint8_t* __restrict__ qo,
+                                                             uint8_t* __restrict__ so) {
+  const Idx total = R * (K / 16);
+  const Idx nslab = K / 64;
+  const Idx gpr = K / 32;
+  for (Idx u = (Idx)blockIdx.x * kThreads + threadIdx.x; u < total; u += (Idx)gridDim.x * kThreads) {
+    const Idx t = u & 7, rest = u >> 3;
+    const Idx sl = rest % nslab, pair = rest / nslab;
+    const Idx row = 2 * pair + (t >> 2), c = t & 3;
+    const bool in = row < rows;
+    const i32x4 v = in ? *(const i32x4*)(q + (size_t)row * K + sl * 64 + c * 16) : i32x4{0, 0, 0, 0};
+    *(i32x4*)(qo + (size_t)sl * R * 64 + (size_t)pair * 128 + t * 16) = v;
+    if (c == 0) {
+      const uint16_t sc = in ? *(const uint16_t*)(s + (size_t)row * gpr + 2 * sl) : (uint16_t)0;
+      *(uint16_t*)(so + (size_t)sl * R * 2 + (size_t)row * 2) = sc;
+    }
+  }
+}
+
+int64_t grid_for(int64_t units, int64_t per_block) {
+  int64_t blocks = (units + per_block - 1) / per_block;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  if (total < (int64_t)1 << 31 && rows * ld < (int64_t)1 << 31) {
-    hipLaunchKernelGGL((quantize_kernel<F32, uint32_t>), dim3((unsigned)blocks), dim3(kThreads), 0, st, x,
-                       (uint32_t)rows, (uint32_t)K, (uint32_t)ld, q, s);
+  return blocks;
+}
+
+template <bool F32, bool SLAB>
+hipError_t launch_typed(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s, hipStream_t st) {
+  const int64_t R = SLAB ? slab_rows(rows) : rows;
+  const int64_t total = R * (K / 8);
+  const unsigned blocks = (unsigned)grid_for(total, (int64_t)kThreads * kItems);
+  if (total < (int64_t)1 << 31 && rows * ld < (int64_t)1 << 31 && R * K < (int64_t)1 << 31) {
+    hipLaunchKernelGGL((quantize_kernel<F32, SLAB, uint32_t>), dim3(blocks), dim3(kThreads), 0, st, x,
+                       (uint32_t)rows, (uint32_t)K, (uint32_t)ld, (uint32_t)R, q, s);
   } else {
-    hipLaunchKernelGGL((quantize_kernel<F32, uint64_t>), dim3((unsigned)blocks), dim3(kThreads), 0, st, x,
-                       (uint64_t)rows, (uint64_t)K, (uint64_t)ld, q, s);
+    hipLaunchKernelGGL((quantize_kernel<F32, SLAB, uint64_t>), dim3(blocks), dim3(kThreads), 0, st, x,
+                       (uint64_t)rows, (uint64_t)K, (uint64_t)ld, (uint64_t)R, q, s);
   }
   return hipGetLastError();
 }
@@ -89,8 +139,29 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t K, int64_t ld, uint
 
 hipError_t launch_quantize(int kind, const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s,
                            hipStream_t stream) {
-  return kind == 1 ? launch_typed<true>(x, rows, K, ld, q, s, stream)
-                   : launch_typed<false>(x, rows, K, ld, q, s, stream);
+  return kind == 1 ? launch_typed<true, false>(x, rows, K, ld, q, s, stream)
+                   : launch_typed<false, false>(x, rows, K, ld, q, s, stream);
+}
+
+hipError_t launch_quantize_slab(int kind, const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s,
+                                hipStream_t stream) {
+  return kind == 1 ? launch_typed<true, true>(x, rows, K, ld, q, s, stream)
+                   : launch_typed<false, true>(x, rows, K, ld, q, s, stream);
+}
+
+hipError_t launch_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, uint8_t* qo, uint8_t* so,
+                            hipStream_t stream) {
+  const int64_t R = slab_rows(rows);
+  const int64_t total = R * (K / 16);
+  const unsigned blocks = (unsigned)grid_for(total, (int64_t)kThreads * 4);
+  if (R * K < (int64_t)1 << 31) {
+    hipLaunchKernelGGL((slab_pack_kernel<uint32_t>), dim3(blocks), dim3(kThreads), 0, stream, q, s, (uint32_t)rows,
+                       (uint32_t)K, (uint32_t)R, qo, so);
+  } else {
+    hipLaunchKernelGGL((slab_pack_kernel<uint64_t>), dim3(blocks), dim3(kThreads), 0, stream, q, s, (uint64_t)rows,
+                       (uint64_t)K, (uint64_t)R, qo, so);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace mx

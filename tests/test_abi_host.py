@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 1
+    assert L.mx_abi_version() == 2
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -105,6 +105,40 @@ def test_linear_rejects_bad_arguments(L):
     q = L.mx_linear_q
     assert q(P(A), P(0), 8, 64, P(B), P(C), 256, P(0), 0, P(D), P(0)) == 1  # NULL xs
     assert q(P(A), P(C + 64), 8, 64, P(B), P(C), 256, P(0), 0, P(A), P(0)) == 1  # y overlaps xq
+
+
+def test_slab_rows(L):
+    assert [L.mx_slab_rows(r) for r in (0, 1, 255, 256, 257, 75348)] == [0, 256, 256, 256, 512, 75520]
+    assert L.mx_slab_rows(-1) == -1
+
+
+def test_slab_calls_reject_bad_arguments(L):
+    qs = L.mx_quantize_act_slab
+    assert qs(P(A), 4, 96, 96, P(B), P(C), P(0)) == 1  # K % 64
+    assert qs(P(A), 4, 64, 64, P(B), P(0), P(0)) == 1  # NULL s
+    # codes of a slab cover R = 256 rows: 256 * 64 bytes from B; scales at B + 8192 overlap them
+    assert qs(P(A), 4, 64, 64, P(B), P(B + 8192), P(0)) == 1
+    assert qs(P(A), 0, 64, 64, P(0), P(0), P(0)) == 0
+    qw = L.mx_quantize_weight_slab
+    assert qw(P(A), 1, 4, 32, 32, P(B), P(C), P(0)) == 1  # K % 64
+    assert qw(P(A), 9, 4, 64, 64, P(B), P(C), P(0)) == 1  # dtype
+    pk = L.mx_slab_pack
+    assert pk(P(A), P(C), 4, 96, P(B), P(D), P(0)) == 1  # K % 64
+    assert pk(P(A), P(C + 1), 4, 64, P(B), P(D), P(0)) == 1  # odd scale address
+    assert pk(P(A), P(C), 4, 64, P(A + 128), P(D), P(0)) == 1  # output overlaps input
+    assert pk(P(A), P(C), 0, 64, P(0), P(0), P(0)) == 0
+    ls = L.mx_linear_slab
+
+    def lsl(xq=A, xs=C, M=8, K=64, wq=B, ws=C + 0x100000, N=256, bias=0, epi=0, y=D):
+        return ls(P(xq), P(xs), M, K, P(wq), P(ws), N, P(bias), epi, P(y), P(0))
+
+    assert lsl(K=96) == 1
+    assert lsl(epi=3) == 1
+    assert lsl(xs=C + 2) == 1  # scales 4-byte aligned
+    assert lsl(xq=0) == 1
+    assert lsl(y=A + 8192) == 1  # y overlaps the token slab (256 rows x 64 B)
+    assert lsl(N=264) == 2
+    assert lsl(M=0) == 0 and lsl(N=0) == 0
 
 
 def test_forced_unsupported_path(L, monkeypatch):

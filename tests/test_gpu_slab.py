@@ -1,0 +1,220 @@
+"""GPU parity of the slab-layout path (mx_quantize_act_slab,
+mx_quantize_weight_slab, mx_slab_pack, mx_linear_slab) against the oracle.
+
+The slab layout only moves bytes: codes [K/64][R][64] and scales
+[K/64][R][2] with R the row count rounded up to 256 and zero pad rows. The
+oracle's row-major codes and scales are placed in that layout here, on the
+host, and compared byte for byte; the GEMM is held to the same tolerance as
+the row-major one (1e-3 g sum|a||b| + one bf16 ulp) and must equal
+mx_linear_q bit for bit, since it performs the same MFMAs in the same order.
+
+Source of the rule: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound
+OptRTN)", section "Quantization Details".
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_linear_close, dev, f64, mx, quant_ref, u8
+
+pytestmark = pytest.mark.gpu
+
+
+def to_slab(q, s):
+    """Row-major numpy codes [rows, K] and scales [rows, K/32] in the slab layout."""
+    rows, K = q.shape
+    R = (rows + 255) // 256 * 256
+    qs = np.zeros((K // 64, R, 64), dtype=np.uint8)
+    ss = np.zeros((K // 64, R, 2), dtype=np.uint8)
+    qs[:, :rows] = q.reshape(rows, K // 64, 64).transpose(1, 0, 2)
+    ss[:, :rows] = s.reshape(rows, K // 64, 2).transpose(1, 0, 2)
+    return qs, ss
+
+
+def slab_rows_of(sl, rows):
+    """Row-major codes and scales of the given rows of a Slab (numpy)."""
+    q = u8(sl.q[:, rows])  # [K/64, n, 64]
+    s = u8(sl.s[:, rows])
+    n = len(rows)
+    return q.transpose(1, 0, 2).reshape(n, -1), s.transpose(1, 0, 2).reshape(n, -1)
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (77, 192), (256, 128), (300, 5120), (513, 640)])
+def test_act_slab_quantizer_matches_oracle(M, K):
+    x = synth.make_activation(M, K, seed=M + 3 * K)
+    sl = mx().mx_quantize_act_slab(x.to(dev()))
+    rq, rs = to_slab(*quant_ref(x))
+    assert np.array_equal(u8(sl.s), rs)
+    assert np.array_equal(u8(sl.q), rq)
+
+
+def test_act_slab_quantizer_strided_rows_and_nonfinite():
+    base = synth.make_activation(70, 384, seed=9)
+    base[3, 70] = float("nan")
+    base[5, 200] = float("-inf")
+    x = base.to(dev())[:, 64:320]  # pitch 384, K 256
+    sl = mx().mx_quantize_act_slab(x)
+    rq, rs = to_slab(*quant_ref(base[:, 64:320]))
+    assert np.array_equal(u8(sl.s), rs) and np.array_equal(u8(sl.q), rq)
+
+
+def test_act_slab_quantizer_full_size_sampled_rows():
+    M, K = synth.VIDEO_TOKENS, synth.HIDDEN
+    x = synth.make_activation(M, K, seed=0)
+    print(f"full-size slab act quantize {M}x{K}", flush=True)
+    sl = mx().mx_quantize_act_slab(x.to(dev()))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 90, M), rng.integers(0, M, 512)]))
+    q, s = slab_rows_of(sl, torch.from_numpy(rows))
+    rq, rs = oracle.quantize_mx(f64(x[rows]))
+    assert np.array_equal(s, rs) and np.array_equal(q, rq)
+    R = sl.q.shape[1]
+    assert R == 75520
+    assert not sl.q[:, M:].any() and not sl.s[:, M:].any()  # pad rows are zero
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_weight_slab_quantizer_matches_oracle(dtype):
+    w = synth.make_weight(272, 1024, seed=4).to(dtype)
+    w[7, 9] = float("inf")
+    sl = mx().mx_quantize_weight_slab(w.to(dev()))
+    rq, rs = to_slab(*quant_ref(w))
+    assert np.array_equal(u8(sl.s), rs) and np.array_equal(u8(sl.q), rq)
+
+
+def test_slab_pack_matches_slab_quantizer():
+    w = synth.make_weight(600, 640, seed=6).to(dev())
+    q, s = mx().mx_quantize_weight(w)
+    a = mx().mx_slab_pack(q, s)
+    b = mx().mx_quantize_weight_slab(w)
+    torch.cuda.synchronize()
+    assert torch.equal(a.q, b.q) and torch.equal(a.s, b.s)
+
+
+def run_slab(M, K, N, seed, bias=True, gelu=False, x=None):
+    d = dev()
+    x = synth.make_activation(M, K, seed) if x is None else x
+    w = synth.make_weight(N, K, seed)
+    b = synth.make_bias(N, seed) if bias else None
+    ws = mx().mx_quantize_weight_slab(w.to(d))
+    xs = mx().mx_quantize_act_slab(x.to(d))
+    y = mx().mx_linear_slab(xs, ws, None if b is None else b.to(d), gelu=gelu)
+    torch.cuda.synchronize()
+    return x, w, b, y
+
+
+def oracle_linear(x, w, b, gelu):
+    xq, xs = quant_ref(x)
+    wq, ws = quant_ref(w)
+    return oracle.linear_ref(xq, xs, wq, ws, bias=None if b is None else f64(b),
+                             epilogue="gelu_tanh" if gelu else "none")
+
+
+@pytest.mark.parametrize(
+    "M,K,N",
+    [(1, 64, 16), (5, 64, 32), (77, 192, 256), (256, 128, 256), (300, 320, 512), (513, 512, 272), (70, 5120, 768)],
+)
+def test_linear_slab_small_shapes(M, K, N):
+    print(f"linear_slab M={M} K={K} N={N}", flush=True)
+    x, w, b, y = run_slab(M, K, N, seed=M * 5 + K + N)
+    yref, S = oracle_linear(x, w, b, False)
+    assert_linear_close(y, yref, S, what=f"M{M} K{K} N{N}")
+
+
+def test_linear_slab_gelu_no_bias():
+    x, w, b, y = run_slab(300, 448, 512, seed=12, bias=False, gelu=True)
+    yref, S = oracle_linear(x, w, None, True)
+    assert_linear_close(y, yref, S, "gelu_tanh", what="gelu")
+
+
+@pytest.mark.parametrize("gelu", [False, True])
+def test_linear_slab_equals_row_major_bitwise(gelu):
+    d = dev()
+    x = synth.make_activation(600, 1024, seed=31).to(d)
+    w = synth.make_weight(512, 1024, seed=31).to(d)
+    b = synth.make_bias(512, seed=31).to(d)
+    wq, ws = mx().mx_quantize_weight(w)
+    xq, xs = mx().mx_quantize_act(x)
+    y1 = mx().mx_linear_q(xq, xs, wq, ws, b, gelu=gelu)
+    y2 = mx().mx_linear_slab(mx().mx_slab_pack(xq, xs), mx().mx_slab_pack(wq, ws), b, gelu=gelu)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_linear_slab_zero_rows_give_bias():
+    ctx = synth.make_text_context(512, 5120, seed=2)
+    x, w, b, y = run_slab(512, 5120, 1024, seed=2, x=ctx)
+    want = f64(b.float().to(torch.bfloat16))
+    assert np.array_equal(f64(y)[410:], np.broadcast_to(want, (102, 1024)))
+    yref, S = oracle_linear(x, w, b, False)
+    assert_linear_close(y, yref, S, what="text ctx")
+
+
+def test_linear_slab_deterministic_and_fully_written():
+    d = dev()
+    xs = mx().mx_quantize_act_slab(synth.make_activation(333, 512, seed=21).to(d))
+    ws = mx().mx_quantize_weight_slab(synth.make_weight(768, 512, seed=21).to(d))
+    y1 = torch.full((333, 768), float("nan"), dtype=torch.bfloat16, device=d)
+    y2 = torch.full((333, 768), float("nan"), dtype=torch.bfloat16, device=d)
+    mx().mx_linear_slab(xs, ws, y=y1)
+    mx().mx_linear_slab(xs, ws, y=y2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y1).any()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def sampled_rows(M, n=96, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(4), np.arange(M - 84, M), rng.integers(0, M, n)]))
+
+
+def test_linear_slab_qkv_full_size():
+    d = dev()
+    shp = synth.CONFIGS["qkv_75348x5120x15360"][0]
+    x = synth.make_activation(shp.M, shp.K, 100)
+    w = synth.make_weight(shp.N, shp.K, 100)
+    b = synth.make_bias(shp.N, 100)
+    print(f"slab qkv {shp}", flush=True)
+    xd, wd, bd = x.to(d), w.to(d), b.to(d)
+    ws = mx().mx_quantize_weight_slab(wd)
+    y = mx().mx_linear_slab(mx().mx_quantize_act_slab(xd), ws, bd)
+    wq, wsr = mx().mx_quantize_weight(wd)
+    xq, xsr = mx().mx_quantize_act(xd)
+    y_rm = mx().mx_linear_q(xq, xsr, wq, wsr, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_rm.view(torch.int16))
+    del y_rm, xq, xsr
+    rows = sampled_rows(shp.M)
+    yref, S = oracle.linear_ref(*quant_ref(x[rows]), u8(wq), u8(wsr), bias=f64(b))
+    assert_linear_close(y[rows], yref, S, what="qkv slab")
+
+
+def test_ffn_chain_full_size_slab():
+    # ffn.net.0.proj (GELU) then ffn.net.2 over all 75348 tokens: the bf16
+    # intermediate h [75348, 13824] is quantized again into a slab of 216
+    # K-slabs (offsets past 2^30 bytes). Down-projection rows are checked
+    # against the oracle on the quantization of the GPU's own h.
+    d = dev()
+    up, down = synth.CONFIGS["ffn_75348x5120x13824"]
+    print(f"slab ffn {up} -> {down}", flush=True)
+    x = synth.make_activation(up.M, up.K, 7)
+    w1, b1 = synth.make_weight(up.N, up.K, 7), synth.make_bias(up.N, 7)
+    w2, b2 = synth.make_weight(down.N, down.K, 8), synth.make_bias(down.N, 8)
+    w1s = mx().mx_quantize_weight_slab(w1.to(d))
+    w2s = mx().mx_quantize_weight_slab(w2.to(d))
+    h = mx().mx_linear_slab(mx().mx_quantize_act_slab(x.to(d)), w1s, b1.to(d), gelu=True)
+    hs = mx().mx_quantize_act_slab(h)
+    y = mx().mx_linear_slab(hs, w2s, b2.to(d))
+    torch.cuda.synchronize()
+    rows = sampled_rows(up.M, 48, seed=3)
+    hq, hsc = slab_rows_of(hs, torch.from_numpy(rows))
+    rq, rs = quant_ref(h[rows])
+    assert np.array_equal(hsc, rs) and np.array_equal(hq, rq)
+    href, S1 = oracle_linear(x[rows], w1, b1, True)
+    assert_linear_close(h[rows], href, S1, "gelu_tanh", what="ffn up")
+    yref, S2 = oracle.linear_ref(rq, rs, *quant_ref(w2), bias=f64(b2))
+    assert_linear_close(y[rows], yref, S2, what="ffn down")
