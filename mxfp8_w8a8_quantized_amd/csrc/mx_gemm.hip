@@ -7,7 +7,7 @@
 // dynamic activations, F16 biases; FP32 accumulation as in the FP32-accum
 // FP8 mode of "Model Quantization Techniques", Conv3D mode table.)
 //
-// Two kernels, both with 256 (weight rows n) x 256 (tokens m) output tiles,
+// Three kernels, all with 256 (weight rows n) x 256 (tokens m) output tiles,
 // the weights as the MFMA's A operand (a lane's accumulators are consecutive
 // n of one token m) and the E8M0 scales handed straight to the MFMA:
 //
@@ -15,8 +15,10 @@
 //   prologue (FUSED) that quantizes the bf16 token tile inside the K loop.
 //   4 waves, each a 128 x 128 sub-tile of v_mfma_scale_f32_16x16x128_f8f6f4,
 //   operands staged global -> registers -> LDS, two 128-K stages.
-// * pp::linear_prequant_pp (fast path): K % 128 == 0 and pre-quantized
-//   tokens; see its own comment.
+// * pp::linear_prequant_pp: row-major pre-quantized operands with
+//   K % 128 == 0; see its own comment.
+// * slab::linear_slab_kernel: operands in the slab layout of mx.h (the
+//   fastest path); see its own comment.
 //
 // 16x16x128 operand layout (32 bytes per lane in two 16-byte halves, found
 // on the device): lane l holds row l%16, K bytes [16*(l/16), +16) in its
@@ -436,13 +438,13 @@ __device__ __forceinline__ void mma8(f32x16 (&acc)[4][2], const Frags& F) {
   });
 }
 
-// Output of a wave's 128 (n) x 64 (m) tile: bias, epilogue and bf16
-// rounding into LDS staging ([m][n] bf16, 64 rows of 256 B, 8-byte block nb
-// of row m at nb ^ (m & 31), so 32 lanes writing 32 consecutive rows hit 32
+// Output of a wave's 128 (n) x 32 MF (m) tile: bias, epilogue and bf16
+// rounding into LDS staging ([m][n] bf16, rows of 256 B, 8-byte block nb of
+// row m at nb ^ (m & 31), so 32 lanes writing 32 consecutive rows hit 32
 // distinct bank pairs), then 2 rows x 256 B per store instruction with
 // non-temporal stores: whole 128-byte lines, no partial-line writebacks.
-template <int EPI>
-__device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][2], const Params& p, uint8_t* ep, int m0, int n0,
+template <int EPI, int MF = 2>
+__device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Params& p, uint8_t* ep, int m0, int n0,
                                             int rows_m, int rows_n, int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -458,7 +460,7 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][2], const Par
         for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, bp[r]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < MF; ++j) {
         const int m = 32 * j + r32;
         float v[4];
 #pragma unroll
@@ -475,10 +477,10 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][2], const Par
   const int nl = wn * 128 + 4 * r32;
   const bool n_ok = nl < rows_n;
 #pragma unroll 8
-  for (int it = 0; it < 32; ++it) {
+  for (int it = 0; it < 16 * MF; ++it) {
     const int m = 2 * it + hi;
     const i32x2 v = *(const i32x2*)(ep + m * 256 + ((r32 ^ (m & 31)) << 3));
-    const int off = n_ok ? ((wm * 64 + m) * N + n0 + nl) * 2 : kDropOffset;
+    const int off = n_ok ? ((wm * 32 * MF + m) * N + n0 + nl) * 2 : kDropOffset;
     __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0, kStoreAux);
   }
 }
@@ -561,16 +563,19 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
 // cache-line requests per byte (the row-major scales alone cost as many line
 // lookups as all the codes) and lets the loads stream from whole lines.
 //
-// 8 waves and the same 128 (n) x 64 (m) wave sub-tiles and epilogue as the
-// pp kernel. K advances in half-steps of 64 through a ring of 4 LDS regions;
-// waves 0..3 issue the refill of half-step j+4 right after the barrier of
-// half-step j, so each load has three half-steps (about 3000 cycles at full
-// MFMA rate) to land, and about 100 KB per CU are in flight:
+// Four waves of 128 (n) x 128 (m), one per SIMD, 256 accumulators each in
+// AGPRs. Per 64-K half-step a wave reads 256 fragment rows (4 A + 4 B) for
+// 16 MFMAs: 1 KB of LDS per MFMA, against 1.5 KB for eight 128 x 64 waves,
+// so the CU's LDS traffic per half-step is 97 KB (64 KB of reads, 33 KB of
+// DMA writes) instead of 129 KB, which also lowers power and so raises the
+// clock a little. K advances through a ring of 4 LDS regions; each wave
+// issues a quarter of the refill of half-step j+4 in half-step j, so a load
+// has three half-steps to land and about 100 KB per CU are in flight:
 //
 //   half-step j:  wait for this wave's loads of j+1, barrier;
-//                 (loader waves) issue the loads of j+4 into region j % 4;
-//                 8 MFMAs on the fragments of j (registers), with the LDS
-//                 reads of the fragments of j+1 (region (j+1) % 4).
+//                 16 MFMAs on the fragments of j (registers), with the LDS
+//                 reads of the fragments of j+1 (region (j+1) % 4) and then
+//                 the loads of j+4 into region j % 4 between them.
 //
 // Region layout: weight codes 256 rows x 64 B, 16-byte chunk c of row r at
 // slot c ^ ((r >> 2) & 3) (conflict-free for 16-lane phases of b128 reads);
@@ -578,13 +583,11 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
 // the last half-step use an empty resource and write zeros that nobody reads.
 namespace slab {
 
-constexpr int NT8 = 512;
+constexpr int NT4 = 256;
 constexpr int R_W = 0, R_X = 16384, R_WS = 32768, R_XS = 33280;
 constexpr int REGION = 33792;
 constexpr int LDS = 4 * REGION;
-constexpr int LOADS_PER_HALF = 9;  // per loader wave: 4 + 4 code DMAs, 1 scale DMA
-
-using pp::Frags;
+constexpr int LOADS_PER_HALF = 9;  // per wave: 4 + 4 code DMAs, 1 scale DMA
 
 struct Src {
   const uint8_t* w;  // tile origin in slab 0: codes, then scales
@@ -596,7 +599,7 @@ struct Src {
   int voff;                 // lane part of a code DMA offset
 };
 
-// Loads of half-step j by loader wave `wave` (0..3): 16-row blocks 4 wave ..
+// Loads of half-step j by wave `wave` (0..3): 16-row blocks 4 wave ..
 // 4 wave + 3 of both code operands (1 KB each; lane L takes row L/4, global
 // chunk (L%4) ^ (L/16) into LDS slot L%4) and one 256-byte half of the
 // weight (waves 0, 1) or token (waves 2, 3) scales.
@@ -619,6 +622,13 @@ __device__ __forceinline__ void issue_half(const Src& S, uint8_t* smem, int j, i
   }
 }
 
+struct Frags {
+  i32x8 a[4];  // weights: rows wn*128 + 32 f + l%32
+  i32x8 b[4];  // tokens:  rows wm*128 + 32 f + l%32
+  int sa[4];
+  int sb[4];
+};
+
 // Fragments of a region for the 32x32x64 MFMA: lane l, fragment f reads row
 // base + 32 f + l%32, K bytes [16 (l/32), +16) and [32 + 16 (l/32), +16) of
 // the 64, and the scale of group l/32 of the half-step.
@@ -635,8 +645,8 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
     F.sa[f] = reg[R_WS + row * 2 + hi];
   }
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int row = wm * 64 + 32 * f + r32;
+  for (int f = 0; f < 4; ++f) {
+    const int row = wm * 128 + 32 * f + r32;
     const uint8_t* rb = reg + R_X + row * 64;
     const i32x4 b0 = *(const i32x4*)(rb + c0), b1 = *(const i32x4*)(rb + c1);
     F.b[f] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -644,40 +654,45 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
   }
 }
 
-// Half-step j: publish region (j+1) % 4, refill region j % 4 with half-step
-// j+4 (loader waves), MFMAs of j from `cur` while `nxt` is read from region
-// (j+1) % 4. The lgkmcnt(0) in the wait keeps any wave's refill from
-// overtaking another wave's last reads of the region being refilled.
-template <bool LOADER>
-__device__ __forceinline__ void half_step(f32x16 (&acc)[4][2], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
+__device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const Frags& F) {
+  static_for<0, 4>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    static_for<0, 4>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, F.sa[i], 0, F.sb[j]);
+    });
+  });
+}
+
+// Half-step j. The lgkmcnt(0) in the wait keeps any wave's refill from
+// overtaking another wave's last reads of the region being refilled. The LDS
+// reads of the next fragments come first in program order (the compiler
+// keeps DMA writes and LDS reads in order, as it cannot tell the regions
+// apart), two after each of the first 12 MFMAs; the refill DMAs follow in
+// the last four MFMA slots. With one wave per SIMD these groups are what
+// keeps the MFMA pipe fed.
+__device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
                                           int j, int wave, int wn, int wm, int lane) {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS_PER_HALF) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (LOADER) issue_half(S, smem, j + 4, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
   read_frags(nxt, smem + ((j + 1) & 3) * REGION, wn, wm, lane);
-  pp::mma8(acc, cur);
-}
-
-// The K loop, one copy for loader and one for compute-only waves, so that no
-// branch splits a half-step (a split lets the compiler sink the MFMAs of one
-// half-step past the next barrier). Both copies pass the same barriers.
-template <bool LOADER>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[4][2], Frags& F0, Frags& F1, const Src& S, uint8_t* smem,
-                                       int wave, int wn, int wm, int lane) {
-  const int nh = S.nh;
-  int j = 0;
-  for (; j + 1 < nh; j += 2) {
-    half_step<LOADER>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
-    half_step<LOADER>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
-  }
-  if (j < nh) half_step<LOADER>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+  issue_half(S, smem, j + 4, wave, lane);
+  mma16(acc, cur);
+  static_for<0, 16>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (i < 12)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    else
+      __builtin_amdgcn_sched_group_barrier(0x020, i == 12 ? 3 : 2, 0);  // refill DMAs
+  });
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int EPI>
-__global__ __launch_bounds__(NT8, 1) void linear_slab_kernel(Params p) {
+__global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -687,7 +702,6 @@ __global__ __launch_bounds__(NT8, 1) void linear_slab_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const bool loader = wave < 4;
 
   Src S;
   S.w_slab = (uint64_t)p.tiles_n * BN * 64;
@@ -699,32 +713,33 @@ __global__ __launch_bounds__(NT8, 1) void linear_slab_kernel(Params p) {
   S.nh = p.K >> 6;
   S.voff = (lane >> 2) * 64 + (((lane & 3) ^ (lane >> 4)) << 4);
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  if (loader) {
-    issue_half(S, smem, 0, wave, lane);
-    issue_half(S, smem, 1, wave, lane);
-    issue_half(S, smem, 2, wave, lane);
-    issue_half(S, smem, 3, wave, lane);
-  }
+  issue_half(S, smem, 0, wave, lane);
+  issue_half(S, smem, 1, wave, lane);
+  issue_half(S, smem, 2, wave, lane);
+  issue_half(S, smem, 3, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * LOADS_PER_HALF) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   Frags F0, F1;
   read_frags(F0, smem, wn, wm, lane);
-  if (loader)
-    k_loop<true>(acc, F0, F1, S, smem, wave, wn, wm, lane);
-  else
-    k_loop<false>(acc, F0, F1, S, smem, wave, wn, wm, lane);
+  const int nh = S.nh;
+  int j = 0;
+  for (; j + 1 < nh; j += 2) {
+    half_step(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+    half_step(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
+  }
+  if (j < nh) half_step(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  pp::store_tile8<EPI>(acc, p, smem + wave * 16384, m0, n0, rows_m, rows_n, wn, wm, lane);
+  pp::store_tile8<EPI, 4>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
 
 template <int EPI>
@@ -736,7 +751,7 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT8), LDS, st, p);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT4), LDS, st, p);
   return hipGetLastError();
 }
 
