@@ -125,6 +125,54 @@ def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
     }
 
 
+def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
+    """The other Wan2.2-A14B linears on the slab path, one step each: every
+    linear quantizes its activation into a slab and runs the GEMM; the FFN's
+    down-projection takes the up-projection's bf16 GELU output. Inputs are
+    drawn on the GPU (same recipe as the headline's, other seed)."""
+    res = {}
+    for name, shapes in synth.CONFIGS.items():
+        if name == WORKLOAD:
+            continue
+        layers = []
+        for li, shp in enumerate(shapes):
+            seed = 500 + li
+            w = mx.mx_quantize_weight_slab(synth.make_weight_device(shp.N, shp.K, seed, dev))
+            b = synth.make_bias(shp.N, seed).to(dev)
+            layers.append((shp, w, b))
+        acts = []
+        for li, (shp, w, b) in enumerate(layers):
+            if shp.name == "ffn.net.2":
+                acts.append(None)  # the previous layer's output
+                continue
+            if shp.M == synth.TEXT_TOKENS:
+                x = synth.make_text_context(shp.M, shp.K, 500 + li).to(dev)
+            else:
+                x = synth.make_activation_device(shp.M, shp.K, 500 + li, dev)
+            acts.append(x)
+        outs = [torch.empty((shp.M, shp.N), dtype=torch.bfloat16, device=dev) for shp, _, _ in layers]
+        slabs = [None] * len(layers)
+
+        def run():
+            for li, (shp, w, b) in enumerate(layers):
+                x = acts[li] if acts[li] is not None else outs[li - 1]
+                slabs[li] = mx.mx_quantize_act_slab(x, slabs[li])
+                mx.mx_linear_slab(slabs[li], w, b, gelu=shp.gelu, y=outs[li])
+
+        total, _ = timed_step(torch, [run], steps, warmup)
+        ms = total / steps
+        flop = sum(2.0 * shp.M * shp.N * shp.K for shp, _, _ in layers)
+        res[name] = {
+            "linears": [f"{shp.name} {shp.M}x{shp.K}x{shp.N}" + (" gelu" if shp.gelu else "") for shp, _, _ in layers],
+            "ms": round(ms, 4),
+            "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
+            "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
+        }
+        del layers, acts, outs, slabs
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -260,8 +308,12 @@ def main():
             "quantize_weight_GBps": round(w_bytes / (wqa * 1e-3) / 1e9, 1),
         }
 
+    if not args.no_extra:
+        del y
+        out["extra"]["other_workloads"] = other_workloads(torch, mx, synth, dev)
+
     if not args.no_cpu_baseline:
-        del x, y, xsl, rowmajor
+        del x, xsl, rowmajor
         out["cpu_baseline"] = cpu_baseline(x_cpu, w_cpu, b_cpu, CPU_SAMPLE_ROWS)
 
     print(json.dumps(out), flush=True)

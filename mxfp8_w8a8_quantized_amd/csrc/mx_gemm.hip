@@ -475,6 +475,11 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Pa
       }
     }
   }
+  // The staging rows pass data between lanes. Seen from one lane, the reads
+  // below touch addresses it never wrote, so without this barrier the
+  // compiler may move them above the other lanes' writes (it did, in an
+  // eight-pass variant); the hardware keeps LDS order within a wave.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const int N = p.N;
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + (size_t)m0 * N, (uint32_t)(rows_m * N * 2));
   const int nl = wn * 128 + 4 * r32;

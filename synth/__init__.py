@@ -4,6 +4,8 @@ This module holds no arithmetic of the quantization method: it only draws
 random tensors with ``torch.Generator('cpu')`` (so every caller sees the same
 bytes for the same seed) and casts them to the dtypes the layer takes. Both
 the oracle's callers and the GPU path's callers use it; it imports neither.
+The ``*_device`` variants draw the same recipe with a seeded generator on a
+GPU, for timing runs whose inputs the oracle never sees.
 
 Shapes (model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
 sections "Quantization Details" and "Running the Official Example"):
@@ -28,8 +30,10 @@ from .inputs import (  # noqa: F401
     LinearShape,
     block_layer_seed,
     make_activation,
+    make_activation_device,
     make_bias,
     make_text_context,
     make_weight,
+    make_weight_device,
     video_tokens,
 )

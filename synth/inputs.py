@@ -54,6 +54,26 @@ def make_activation(M, K, seed, outlier_p=1e-3, outlier_scale=50.0, chunk_rows=4
     return out
 
 
+def make_activation_device(M, K, seed, device, outlier_p=1e-3, outlier_scale=50.0):
+    """The recipe of make_activation drawn with a seeded generator on
+    `device` (other values, same distribution): for timing runs whose inputs
+    the oracle never sees, where drawing 1e9 values on the host is slow."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + SEED_X * 7919)
+    v = torch.randn((M, K), device=device, generator=g)
+    if outlier_p > 0:
+        mask = torch.rand((M, K), device=device, generator=g) < outlier_p
+        v = torch.where(mask, v * outlier_scale, v)
+    return v.to(torch.bfloat16)
+
+
+def make_weight_device(N, K, seed, device, std=0.02, stream=SEED_W):
+    """make_weight's recipe drawn on `device` (see make_activation_device)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + stream * 7919)
+    return torch.randn((N, K), device=device, generator=g) * std
+
+
 def make_text_context(M, K, seed, pad_fraction=TEXT_PAD_FRACTION):
     """bf16 [M, K] ~ N(0,1) with its last floor(pad_fraction * M) rows zero."""
     x = make_activation(M, K, seed, outlier_p=0.0)
