@@ -168,6 +168,21 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
             "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
             "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
         }
+        if [shp.name for shp, _, _ in layers] == ["ffn.net.0.proj", "ffn.net.2"]:
+            # The same pair with the requantization fused into the up-projection.
+            (s1, w1, b1), (s2, w2, b2) = layers
+            hs = [None]
+
+            def run_fused():
+                slabs[0] = mx.mx_quantize_act_slab(acts[0], slabs[0])
+                hs[0] = mx.mx_linear_slab_requant(slabs[0], w1, b1, gelu=s1.gelu, out=hs[0])
+                mx.mx_linear_slab(hs[0], w2, b2, gelu=s2.gelu, y=outs[1])
+
+            total, _ = timed_step(torch, [run_fused], steps, warmup)
+            ms = total / steps
+            res[name]["fused_requant_ms"] = round(ms, 4)
+            res[name]["fused_requant_TFLOPs"] = round(flop / (ms * 1e-3) / 1e12, 2)
+            del hs
         del layers, acts, outs, slabs
         torch.cuda.empty_cache()
     return res

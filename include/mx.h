@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 2
+#define MX_ABI_VERSION 3
 
 typedef enum {
   MX_OK = 0,
@@ -151,6 +151,19 @@ int mx_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
 int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                    const uint8_t* wq, const uint8_t* ws, int64_t N,
                    const void* bias, int epilogue, void* y, void* stream);
+
+/* The same linear, writing instead of y the MX quantization of bf16 y (by
+ * the rule above, bit-identical to mx_quantize_act_slab of mx_linear_slab's
+ * output) in the slab layout of an operand with rows M and K' = N:
+ * hq [N/64][RM][64], hs [N/64][RM][2], RM = mx_slab_rows(M); pad rows are
+ * zero. This is the feed-forward pair of Wan2.2 (ffn.net.0.proj with GELU,
+ * then ffn.net.2 on the requantized intermediate) without the bf16
+ * intermediate in memory. N % 64 == 0 (else MX_ERR_INVALID_ARGUMENT);
+ * RM * N < 2^31 (else MX_ERR_UNSUPPORTED); hq 16-byte aligned; outputs must
+ * not overlap the inputs or each other. */
+int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                           const uint8_t* wq, const uint8_t* ws, int64_t N,
+                           const void* bias, int epilogue, uint8_t* hq, uint8_t* hs, void* stream);
 
 #ifdef __cplusplus
 }

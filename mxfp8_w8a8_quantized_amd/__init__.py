@@ -42,6 +42,7 @@ SIGNATURES = {
     "mx_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_slab_pack": ([_P, _P, _I64, _I64, _P, _P, _P], _INT),
     "mx_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
+    "mx_linear_slab_requant": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _P], _INT),
 }
 
 
@@ -275,8 +276,7 @@ def mx_slab_pack(q, s, out=None):
     return out
 
 
-def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
-    """y = bf16(epi(xhat @ what^T + bias)) on slab operands x (tokens) and w (weights)."""
+def _slab_linear_args(x, w, bias):
     dev = x.q.device
     for name, t in (("x.q", x.q), ("x.s", x.s), ("w.q", w.q), ("w.s", w.s)):
         _need(t, name, torch.uint8, dev)
@@ -291,6 +291,12 @@ def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
         _need(bias, "bias", torch.float16, dev)
         if bias.shape != (N,):
             raise ValueError("bias must be f16 [N]")
+    return dev, M, N, K
+
+
+def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
+    """y = bf16(epi(xhat @ what^T + bias)) on slab operands x (tokens) and w (weights)."""
+    dev, M, N, K = _slab_linear_args(x, w, bias)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
     _need(y, "y", torch.bfloat16, dev)
     if y.shape != (M, N):
@@ -303,3 +309,21 @@ def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
             )
         )
     return y
+
+
+def mx_linear_slab_requant(x, w, bias=None, gelu=False, out=None):
+    """The same linear returning, instead of bf16 y, the Slab of y's MX
+    quantization (rows M, K = N): the next linear's activation operand."""
+    dev, M, N, K = _slab_linear_args(x, w, bias)
+    if N % 64 != 0:
+        raise ValueError("the requantized output needs N % 64 == 0")
+    out = _slab_out(M, N, dev, out)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_slab_requant(
+                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(out.q), _ptr(out.s),
+                _stream(dev),
+            )
+        )
+    return out

@@ -127,6 +127,38 @@ int check_quantize(const void* x, int dt, int64_t rows, int64_t K, int64_t ld, c
   return check_device();
 }
 
+// Slab-linear operand arguments (shared by the bf16 and requantizing outputs).
+int check_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                      const uint8_t* ws, int64_t N, const void* bias, int epilogue) {
+  int st;
+  if ((st = check_rows("M", M)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (K % 64 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
+  if (N < 0) return fail(MX_ERR_INVALID_ARGUMENT, "N = %lld is negative", (long long)N);
+  if (N > kMaxKN) return fail(MX_ERR_UNSUPPORTED, "N = %lld exceeds the supported 2^20", (long long)N);
+  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH)
+    return fail(MX_ERR_INVALID_ARGUMENT, "unknown epilogue %d", epilogue);
+  if (M == 0 || N == 0) return MX_OK;
+  if (N % 16 != 0) return fail(MX_ERR_UNSUPPORTED, "N = %lld must be a multiple of 16", (long long)N);
+  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr)
+    return fail(MX_ERR_INVALID_ARGUMENT, "NULL operand pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xs, 4) || !aligned(ws, 4))
+    return fail(MX_ERR_INVALID_ARGUMENT, "codes must be 16-byte aligned, scales 4-byte aligned");
+  if (bias != nullptr && !aligned(bias, 2)) return fail(MX_ERR_INVALID_ARGUMENT, "bias must be 2-byte aligned");
+  return MX_OK;
+}
+
+// An output range [out, out + bytes) must not overlap any slab-linear input.
+int check_slab_output(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                      const uint8_t* ws, int64_t N, const void* bias, const void* out, uint64_t bytes,
+                      const char* name) {
+  const uint64_t RM = (uint64_t)mx::slab_rows(M), RN = (uint64_t)mx::slab_rows(N);
+  if (overlap(out, bytes, xq, RM * K) || overlap(out, bytes, xs, RM * (K / 32)) || overlap(out, bytes, wq, RN * K) ||
+      overlap(out, bytes, ws, RN * (K / 32)) || overlap(out, bytes, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "%s overlaps an input", name);
+  return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,29 +263,35 @@ int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, cons
 
 int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws,
                    int64_t N, const void* bias, int epilogue, void* y, void* stream) {
-  int st;
-  if ((st = check_rows("M", M)) != MX_OK) return st;
-  if ((st = check_k(K)) != MX_OK) return st;
-  if (K % 64 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
-  if (N < 0) return fail(MX_ERR_INVALID_ARGUMENT, "N = %lld is negative", (long long)N);
-  if (N > kMaxKN) return fail(MX_ERR_UNSUPPORTED, "N = %lld exceeds the supported 2^20", (long long)N);
-  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH)
-    return fail(MX_ERR_INVALID_ARGUMENT, "unknown epilogue %d", epilogue);
-  if (M == 0 || N == 0) return MX_OK;
-  if (N % 16 != 0) return fail(MX_ERR_UNSUPPORTED, "N = %lld must be a multiple of 16", (long long)N);
-  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr || y == nullptr)
-    return fail(MX_ERR_INVALID_ARGUMENT, "NULL operand or output pointer");
-  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(ws, 4))
-    return fail(MX_ERR_INVALID_ARGUMENT, "codes and y must be 16-byte aligned, scales 4-byte aligned");
-  if (bias != nullptr && !aligned(bias, 2)) return fail(MX_ERR_INVALID_ARGUMENT, "bias must be 2-byte aligned");
-  const uint64_t RM = (uint64_t)mx::slab_rows(M), RN = (uint64_t)mx::slab_rows(N);
-  const uint64_t yb = (uint64_t)M * N * 2;
-  if (overlap(y, yb, xq, RM * K) || overlap(y, yb, xs, RM * (K / 32)) || overlap(y, yb, wq, RN * K) ||
-      overlap(y, yb, ws, RN * (K / 32)) || overlap(y, yb, bias, (uint64_t)N * 2))
-    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (y == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL y");
+  if (!aligned(y, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned");
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, y, (uint64_t)M * N * 2, "y")) != MX_OK) return st;
   if ((st = check_device()) != MX_OK) return st;
   (void)hipGetLastError();
   return finish(mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
+                "linear launch");
+}
+
+int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                           const uint8_t* ws, int64_t N, const void* bias, int epilogue, uint8_t* hq, uint8_t* hs,
+                           void* stream) {
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (N % 64 != 0)
+    return fail(MX_ERR_INVALID_ARGUMENT, "N = %lld must be a multiple of 64 (it is the next linear's K)", (long long)N);
+  if (hq == nullptr || hs == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL hq or hs");
+  if (!aligned(hq, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "hq must be 16-byte aligned");
+  const uint64_t RM = (uint64_t)mx::slab_rows(M);
+  if (RM * (uint64_t)N >= (uint64_t(1) << 31))
+    return fail(MX_ERR_UNSUPPORTED, "output slab of %llu bytes exceeds 2^31", (unsigned long long)(RM * N));
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, hq, RM * N, "hq")) != MX_OK) return st;
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, hs, RM * (N / 32), "hs")) != MX_OK) return st;
+  if (overlap(hq, RM * N, hs, RM * (N / 32))) return fail(MX_ERR_INVALID_ARGUMENT, "hq overlaps hs");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear_slab_requant(xq, xs, M, K, wq, ws, N, bias, epilogue, hq, hs, (hipStream_t)stream),
                 "linear launch");
 }
 

@@ -62,6 +62,8 @@ struct Params {
   const uint8_t* ws;
   const uint16_t* bias;  // f16 bits, or null
   uint16_t* y;           // bf16 bits
+  uint8_t* hq;           // requantized output: codes slab [N/64][RM][64] (or null)
+  uint8_t* hs;           //                     scales slab [N/64][RM][2]
   int M, N, K;
   int tiles_m, tiles_n;
 };
@@ -791,7 +793,74 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Requantizing epilogue: instead of y, the MX quantization of y (bf16) in
+// the slab layout, as the next linear takes it (K' = N; the FFN
+// down-projection after the GELU up-projection). The wave's 128 x 128 bf16
+// results are staged in LDS as in the plain epilogue (8-byte block nb of row
+// m at nb ^ ((m & 15) << 1), so that two neighbouring blocks stay adjacent);
+// then each lane reads 8 consecutive values of a row, the 4 lanes of a DPP
+// quad hold one group of 32, and quantize8_bf16 encodes them exactly as the
+// quantizer does. 16 lanes cover a row's 128 values, i.e. two 64-wide
+// K'-slabs; 4 rows per read make whole 256-byte runs in each slab. Rows past
+// M are written as zero codes and scales (the slab's pad rows); columns past
+// N are dropped.
 template <int EPI>
+__device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Params& p, uint8_t* ep, int m0, int n0,
+                                             int rows_n, int wn, int wm, int lane) {
+  const int r32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nb = 8 * i + 2 * q + hi;
+      const int nl = wn * 128 + 4 * nb;
+      float b[4] = {0.f, 0.f, 0.f, 0.f};
+      if (p.bias != nullptr && nl < rows_n) {
+        const uint16_t* bp = p.bias + n0 + nl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, bp[r]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 32 * j + r32;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] + b[r]);
+        const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
+        const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
+        *(i32x2*)(ep + m * 256 + ((nb ^ ((m & 15) << 1)) << 3)) =
+            i32x2{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1)};
+      }
+    }
+  }
+  // The staging rows pass data between lanes (see store_tile8).
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int RM = p.tiles_m * BM;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.hq, (uint32_t)((size_t)RM * p.N));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.hs, (uint32_t)((size_t)RM * (p.N / 32)));
+  const int c = lane & 15;
+  const int ng = n0 + wn * 128 + 8 * c;  // K' index of this lane's first value
+  const bool n_ok = ng < p.N;
+  const int slab = ng >> 6;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = 4 * it + (lane >> 4);
+    const int mg = m0 + wm * 128 + row;
+    i32x4 v = *(const i32x4*)(ep + row * 256 + (((2 * c) ^ ((row & 15) << 1)) << 3));
+    if (mg >= p.M) v = i32x4{0, 0, 0, 0};
+    const uint32_t raw[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+    uint32_t codes[2], sc;
+    quantize8_bf16(raw, codes, sc);
+    const int qo = n_ok ? slab * RM * 64 + mg * 64 + (ng & 63) : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)codes[0], (int)codes[1]}, rq, qo, 0, 0);
+    if ((c & 3) == 0) {
+      const int so = n_ok ? slab * RM * 2 + mg * 2 + ((c >> 2) & 1) : kDropOffset;
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rs, so, 0, 0);
+    }
+  }
+}
+
+template <int EPI, bool QOUT>
 __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
@@ -839,13 +908,16 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  pp::store_tile8<EPI, 4>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
+  if constexpr (QOUT)
+    store_tile_q<EPI>(acc, p, smem + wave * 32768, m0, n0, rows_n, wn, wm, lane);
+  else
+    pp::store_tile8<EPI, 4>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
 
-template <int EPI>
+template <int EPI, bool QOUT = false>
 hipError_t launch(const Params& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
-  auto kern = linear_slab_kernel<EPI>;
+  auto kern = linear_slab_kernel<EPI, QOUT>;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
@@ -889,6 +961,8 @@ hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
   p.ws = ws;
   p.bias = (const uint16_t*)bias;
   p.y = (uint16_t*)y;
+  p.hq = nullptr;
+  p.hs = nullptr;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -911,6 +985,8 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
   p.ws = ws;
   p.bias = (const uint16_t*)bias;
   p.y = (uint16_t*)y;
+  p.hq = nullptr;
+  p.hs = nullptr;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -918,6 +994,27 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
   p.tiles_n = (int)((N + BN - 1) / BN);
   const int nwg = p.tiles_m * p.tiles_n;
   return epi == 1 ? slab::launch<1>(p, nwg, stream) : slab::launch<0>(p, nwg, stream);
+}
+
+hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                      const uint8_t* ws, int64_t N, const void* bias, int epi, uint8_t* hq,
+                                      uint8_t* hs, hipStream_t stream) {
+  Params p;
+  p.x = xq;
+  p.xs = xs;
+  p.wq = wq;
+  p.ws = ws;
+  p.bias = (const uint16_t*)bias;
+  p.y = nullptr;
+  p.hq = hq;
+  p.hs = hs;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const int nwg = p.tiles_m * p.tiles_n;
+  return epi == 1 ? slab::launch<1, true>(p, nwg, stream) : slab::launch<0, true>(p, nwg, stream);
 }
 
 }  // namespace mx

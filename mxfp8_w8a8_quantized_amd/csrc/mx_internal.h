@@ -37,4 +37,11 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
                               const uint8_t* wq, const uint8_t* ws, int64_t N,
                               const void* bias, int epi, void* y, hipStream_t stream);
 
+// The slab GEMM writing, instead of y, the MX quantization of bf16 y in the
+// slab layout with rows M and K' = N: hq [N/64][RM][64], hs [N/64][RM][2],
+// RM = slab_rows(M). N % 64 == 0 and RM * N < 2^31.
+hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                                      const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias,
+                                      int epi, uint8_t* hq, uint8_t* hs, hipStream_t stream);
+
 }  // namespace mx

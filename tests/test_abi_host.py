@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 2
+    assert L.mx_abi_version() == 3
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -139,6 +139,19 @@ def test_slab_calls_reject_bad_arguments(L):
     assert lsl(y=A + 8192) == 1  # y overlaps the token slab (256 rows x 64 B)
     assert lsl(N=264) == 2
     assert lsl(M=0) == 0 and lsl(N=0) == 0
+    rq = L.mx_linear_slab_requant
+
+    def lrq(xq=A, xs=C, M=8, K=64, wq=B, ws=C + 0x100000, N=256, epi=1, hq=D, hs=D + 0x1000000):
+        return rq(P(xq), P(xs), M, K, P(wq), P(ws), N, P(0), epi, P(hq), P(hs), P(0))
+
+    assert lrq(N=272) == 1  # N (the next linear's K) must be a multiple of 64
+    assert lrq(hq=0) == 1 and lrq(hs=0) == 1
+    assert lrq(hq=D + 8) == 1  # misaligned codes
+    assert lrq(hs=D + 1024) == 1  # hs inside hq (256 rows x 256 B)
+    assert lrq(hq=A) == 1  # hq overlaps the token slab
+    assert lrq(K=96) == 1
+    assert lrq(M=1 << 20, N=4096) == 2  # output slab of 2^32 bytes
+    assert lrq(M=0) == 0 and lrq(N=0) == 0
 
 
 def test_forced_unsupported_path(L, monkeypatch):

@@ -1,5 +1,6 @@
 """GPU parity of the slab-layout path (mx_quantize_act_slab,
-mx_quantize_weight_slab, mx_slab_pack, mx_linear_slab) against the oracle.
+mx_quantize_weight_slab, mx_slab_pack, mx_linear_slab,
+mx_linear_slab_requant) against the oracle.
 
 The slab layout only moves bytes: codes [K/64][R][64] and scales
 [K/64][R][2] with R the row count rounded up to 256 and zero pad rows. The
@@ -218,3 +219,51 @@ def test_ffn_chain_full_size_slab():
     assert_linear_close(h[rows], href, S1, "gelu_tanh", what="ffn up")
     yref, S2 = oracle.linear_ref(rq, rs, *quant_ref(w2), bias=f64(b2))
     assert_linear_close(y[rows], yref, S2, what="ffn down")
+
+
+@pytest.mark.parametrize("M,K,N,gelu", [(300, 256, 320, True), (513, 512, 256, False), (70, 5120, 768, True), (1, 64, 64, True)])
+def test_requant_epilogue_equals_two_pass(M, K, N, gelu):
+    # The fused output must be byte-identical to quantizing the bf16 output
+    # of the same GEMM (same accumulation, same bf16 rounding, same rule),
+    # pad rows included.
+    d = dev()
+    xs = mx().mx_quantize_act_slab(synth.make_activation(M, K, seed=M + N).to(d))
+    ws = mx().mx_quantize_weight_slab(synth.make_weight(N, K, seed=M + N).to(d))
+    b = synth.make_bias(N, seed=M + N).to(d)
+    y = mx().mx_linear_slab(xs, ws, b, gelu=gelu)
+    ref = mx().mx_quantize_act_slab(y)
+    out = mx().mx_linear_slab_requant(xs, ws, b, gelu=gelu)
+    torch.cuda.synchronize()
+    assert torch.equal(out.q, ref.q) and torch.equal(out.s, ref.s)
+    assert not out.q[:, M:].any() and not out.s[:, M:].any()
+    # and against the oracle's quantization of the same bf16 values
+    rq, rs = to_slab(*quant_ref(y))
+    assert np.array_equal(u8(out.q), rq) and np.array_equal(u8(out.s), rs)
+
+
+def test_ffn_chain_full_size_fused_requant():
+    # ffn.net.0.proj with GELU writing the requantized intermediate directly,
+    # then ffn.net.2: bit-identical to the two-pass chain, and sampled rows
+    # against the oracle.
+    d = dev()
+    up, down = synth.CONFIGS["ffn_75348x5120x13824"]
+    print(f"slab ffn fused requant {up} -> {down}", flush=True)
+    x = synth.make_activation(up.M, up.K, 17)
+    w1, b1 = synth.make_weight(up.N, up.K, 17), synth.make_bias(up.N, 17)
+    w2, b2 = synth.make_weight(down.N, down.K, 18), synth.make_bias(down.N, 18)
+    w1s = mx().mx_quantize_weight_slab(w1.to(d))
+    w2s = mx().mx_quantize_weight_slab(w2.to(d))
+    xs = mx().mx_quantize_act_slab(x.to(d))
+    hs = mx().mx_linear_slab_requant(xs, w1s, b1.to(d), gelu=True)
+    y = mx().mx_linear_slab(hs, w2s, b2.to(d))
+    h = mx().mx_linear_slab(xs, w1s, b1.to(d), gelu=True)
+    hs2 = mx().mx_quantize_act_slab(h)
+    torch.cuda.synchronize()
+    assert torch.equal(hs.q, hs2.q) and torch.equal(hs.s, hs2.s)
+    del hs2
+    rows = sampled_rows(up.M, 48, seed=5)
+    rq, rs = quant_ref(h[rows])
+    hq, hsc = slab_rows_of(hs, torch.from_numpy(rows))
+    assert np.array_equal(hq, rq) and np.array_equal(hsc, rs)
+    yref, S2 = oracle.linear_ref(rq, rs, *quant_ref(w2), bias=f64(b2))
+    assert_linear_close(y[rows], yref, S2, what="ffn down after fused requant")
