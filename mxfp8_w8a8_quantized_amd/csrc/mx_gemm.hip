@@ -446,8 +446,9 @@ __device__ __forceinline__ void mma8(f32x16 (&acc)[4][2], const Frags& F) {
 // Output of a wave's 128 (n) x 32 MF (m) tile: bias, epilogue and bf16
 // rounding into LDS staging ([m][n] bf16, rows of 256 B, 8-byte block nb of
 // row m at nb ^ (m & 31), so 32 lanes writing 32 consecutive rows hit 32
-// distinct bank pairs), then 2 rows x 256 B per store instruction with
-// non-temporal stores: whole 128-byte lines, no partial-line writebacks.
+// distinct bank pairs), then 4 rows x 256 B per store instruction (16 bytes
+// per lane) with non-temporal stores: whole 128-byte lines, no partial-line
+// writebacks.
 template <int EPI, int MF = 2>
 __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Params& p, uint8_t* ep, int m0, int n0,
                                             int rows_m, int rows_n, int wn, int wm, int lane) {
@@ -484,14 +485,21 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Pa
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const int N = p.N;
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + (size_t)m0 * N, (uint32_t)(rows_m * N * 2));
-  const int nl = wn * 128 + 4 * r32;
+  // 16 bytes (8 values) per lane, 4 rows per store: blocks 2c and 2c + 1 of
+  // row m sit at (2c) ^ s and (2c + 1) ^ s, s = m & 31: one aligned 16-byte
+  // pair, its halves swapped when s is odd.
+  const int c = lane & 15;
+  const int nl = wn * 128 + 8 * c;
   const bool n_ok = nl < rows_n;
 #pragma unroll 8
-  for (int it = 0; it < 16 * MF; ++it) {
-    const int m = 2 * it + hi;
-    const i32x2 v = *(const i32x2*)(ep + m * 256 + ((r32 ^ (m & 31)) << 3));
+  for (int it = 0; it < 8 * MF; ++it) {
+    const int m = 4 * it + (lane >> 4);
+    const int sw = m & 31;
+    const i32x4 v = *(const i32x4*)(ep + m * 256 + ((((2 * c) ^ sw) & ~1) << 3));
+    const bool odd = sw & 1;
+    const i32x4 w = odd ? i32x4{v[2], v[3], v[0], v[1]} : v;
     const int off = n_ok ? ((wm * 32 * MF + m) * N + n0 + nl) * 2 : kDropOffset;
-    __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0, kStoreAux);
+    __builtin_amdgcn_raw_buffer_store_b128(w, ry, off, 0, kStoreAux);
   }
 }
 
