@@ -6,7 +6,7 @@
 // HBM-bound: each lane owns 8 consecutive elements (a quarter of a group of
 // 32), loaded with 16- or 32-byte loads and stored as 8 code bytes; the group
 // maximum is reduced across the four lanes of a DPP quad. Every thread keeps
-// 4 items in flight.
+// 2 items in flight.
 //
 // Row-major output: a wave streams 512 contiguous elements of one row.
 // Slab output (codes [K/64][R][64], scales [K/64][R][2], R = rows rounded up
@@ -20,7 +20,11 @@ namespace mx {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = 4;  // items (8-element quarters) in flight per thread
+// Items (8-element quarters) in flight per thread, and the grid cap: two
+// items with up to 65536 blocks measured best at 75348 x 5120 (0.230 ms,
+// against 0.248 ms for four items with 8192 blocks).
+constexpr int kItems = 2;
+constexpr int64_t kMaxBlocks = 65536;
 
 template <bool F32, bool SLAB, typename Idx>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restrict__ x, Idx rows, Idx K, Idx ld,
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void slab_pack_kernel(const uint8_t* __re
 
 int64_t grid_for(int64_t units, int64_t per_block) {
   int64_t blocks = (units + per_block - 1) / per_block;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
   if (blocks < 1) blocks = 1;
   return blocks;
 }
