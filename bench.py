@@ -285,7 +285,7 @@ def main():
             "M": M,
             "K": K,
             "N": N,
-            "step": "mx_quantize_act_slab + mx_linear_slab (bias, bf16 out)",
+            "step": "mx_quantize_act_slab + mx_linear_slab (bias, bf16 out); the two kernels of mx_linear_ws",
             "pct_of_mxfp8_peak": round(100.0 * value / PEAK_MXFP8_TFLOPS, 2),
         },
         "roofline": {
@@ -306,6 +306,10 @@ def main():
         act_bytes = M * K * (2 + 1 + 1 / 32)
         w_bytes = N * K * (4 + 1 + 1 / 32)
         wqa = mean(wq_per[0])
+        ws_buf = torch.empty((mx.mx_linear_ws_bytes(M, K),), dtype=torch.uint8, device=dev)
+        one_call = lambda: mx.mx_linear_ws(x, wsl, bias, y=y, workspace=ws_buf)  # noqa: E731
+        oc_total, _ = timed_step(torch, [one_call], 10, 2)
+        del ws_buf
         rm_total, (rq_ms, rg_ms) = timed_step(torch, rowmajor, 10, 2)
         _, (f_ms,) = timed_step(torch, [fused], 10, 2)
         fa = mean(f_ms)
@@ -314,6 +318,7 @@ def main():
             "quantize_act_GBps": round(act_bytes / (qa * 1e-3) / 1e9, 1),
             "quantize_act_hbm_frac": round(act_bytes / (qa * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "gemm_ms": round(gemm_ms, 4),
+            "linear_ws_one_call_ms": round(oc_total / 10, 4),
             "rowmajor_step_ms": round(rm_total / 10, 4),
             "rowmajor_step_TFLOPs": round(flop / (rm_total / 10 * 1e-3) / 1e12, 2),
             "rowmajor_gemm_ms": round(mean(rg_ms), 4),

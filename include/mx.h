@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 3
+#define MX_ABI_VERSION 4
 
 typedef enum {
   MX_OK = 0,
@@ -164,6 +164,27 @@ int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
 int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                            const uint8_t* wq, const uint8_t* ws, int64_t N,
                            const void* bias, int epilogue, uint8_t* hq, uint8_t* hs, void* stream);
+
+/* Bytes of workspace mx_linear_ws needs for M token rows and reduction
+ * length K: the activation slab, RM * K codes + RM * K / 32 scales with
+ * RM = mx_slab_rows(M), rounded up to 256 bytes. -1 if M < 0 or K is not a
+ * positive multiple of 64. */
+int64_t mx_linear_ws_bytes(int64_t M, int64_t K);
+
+/* The MXFP8 W8A8 linear in one call on the fast path, activation
+ * quantization included: x bf16 [M][ldx] (ldx >= K, ldx % 8 == 0) is
+ * quantized into `workspace` (its slab layout, mx_quantize_act_slab), then
+ * multiplied by the slab-layout weights wq [K/64][RN][64], ws [K/64][RN][2]
+ * (from mx_quantize_weight_slab or mx_slab_pack) with bias and epilogue into
+ * y bf16 [M][N] (mx_linear_slab). Two kernels on `stream`; nothing is
+ * allocated. workspace: device memory of at least mx_linear_ws_bytes(M, K)
+ * bytes, 256-byte aligned, not overlapping x, the weights, bias or y; it is
+ * overwritten. K % 64 == 0. Same results as mx_linear on the same weights
+ * (bit for bit, when K % 128 == 0). */
+int mx_linear_ws(const void* x, int64_t M, int64_t K, int64_t ldx,
+                 const uint8_t* wq, const uint8_t* ws, int64_t N,
+                 const void* bias, int epilogue, void* y,
+                 void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

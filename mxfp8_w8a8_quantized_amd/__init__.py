@@ -43,6 +43,8 @@ SIGNATURES = {
     "mx_slab_pack": ([_P, _P, _I64, _I64, _P, _P, _P], _INT),
     "mx_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_linear_slab_requant": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _P], _INT),
+    "mx_linear_ws_bytes": ([_I64, _I64], _I64),
+    "mx_linear_ws": ([_P, _I64, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
 }
 
 
@@ -327,3 +329,46 @@ def mx_linear_slab_requant(x, w, bias=None, gelu=False, out=None):
             )
         )
     return out
+
+
+def mx_linear_ws_bytes(M, K):
+    return lib().mx_linear_ws_bytes(M, K)
+
+
+def mx_linear_ws(x, w, bias=None, gelu=False, y=None, workspace=None):
+    """One call on the fast path: bf16 x [M, K] (rows may be strided) is
+    quantized into `workspace` (uint8, >= mx_linear_ws_bytes(M, K) bytes;
+    allocated here when None) and multiplied by the slab weights w."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    dev = x.device
+    M, K = x.shape
+    _need(w.q, "w.q", torch.uint8, dev)
+    _need(w.s, "w.s", torch.uint8, dev)
+    if w.K != K:
+        raise ValueError(f"x has K = {K}, w has K = {w.K}")
+    N = w.rows
+    if bias is not None:
+        _need(bias, "bias", torch.float16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be f16 [N]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    need = mx_linear_ws_bytes(M, K)
+    if need < 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    ld = x.stride(0) if M > 1 else K
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_ws(
+                _ptr(x), M, K, ld, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _ptr(workspace),
+                workspace.numel(), _stream(dev),
+            )
+        )
+    return y

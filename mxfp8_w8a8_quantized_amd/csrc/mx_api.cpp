@@ -295,4 +295,45 @@ int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int6
                 "linear launch");
 }
 
+int64_t mx_linear_ws_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0 || K % 64 != 0 || K > kMaxKN || M > kMaxRows) return -1;
+  const int64_t RM = mx::slab_rows(M);
+  const int64_t bytes = RM * K + RM * (K / 32);
+  return (bytes + 255) / 256 * 256;
+}
+
+int mx_linear_ws(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws, int64_t N,
+                 const void* bias, int epilogue, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
+  // The token slab lives in the workspace: check it as the operand it becomes.
+  const uint64_t RM0 = M > 0 && M <= kMaxRows ? (uint64_t)mx::slab_rows(M) : 0;
+  const uint8_t* wxq = (const uint8_t*)workspace;
+  const uint8_t* wxs = workspace != nullptr && K > 0 ? wxq + RM0 * (uint64_t)K : nullptr;
+  int st = check_linear_slab(wxq, wxs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (x == nullptr || y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x, y or workspace");
+  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
+    return fail(MX_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, workspace 256-byte aligned");
+  const int64_t need = mx_linear_ws_bytes(M, K);
+  if (workspace_bytes < need)
+    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+  const uint64_t RM = (uint64_t)mx::slab_rows(M), RN = (uint64_t)mx::slab_rows(N);
+  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xs = xq + RM * K;
+  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2, ybytes = (uint64_t)M * N * 2;
+  if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, y, ybytes) ||
+      overlap(workspace, need, wq, RN * K) || overlap(workspace, need, ws, RN * (K / 32)) ||
+      overlap(workspace, need, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
+  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, wq, RN * K) || overlap(y, ybytes, ws, RN * (K / 32)) ||
+      overlap(y, ybytes, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  hipError_t e = mx::launch_quantize_slab(0, x, M, K, ldx, xq, xs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return finish(mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
+                "linear launch");
+}
+
 }  // extern "C"

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 3
+    assert L.mx_abi_version() == 4
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -152,6 +152,28 @@ def test_slab_calls_reject_bad_arguments(L):
     assert lrq(K=96) == 1
     assert lrq(M=1 << 20, N=4096) == 2  # output slab of 2^32 bytes
     assert lrq(M=0) == 0 and lrq(N=0) == 0
+
+
+def test_linear_ws_rejects_bad_arguments(L):
+    assert L.mx_linear_ws_bytes(300, 5120) == (512 * 5120 + 512 * 160 + 255) // 256 * 256
+    assert L.mx_linear_ws_bytes(0, 64) == 0
+    assert L.mx_linear_ws_bytes(1, 96) == -1 and L.mx_linear_ws_bytes(-1, 64) == -1
+    f = L.mx_linear_ws
+    need = L.mx_linear_ws_bytes(8, 64)
+    E = 0x50000000
+
+    def call(x=A, M=8, K=64, ldx=64, wq=B, ws=C, N=256, epi=0, y=D, wsp=E, nb=need):
+        return f(P(x), M, K, ldx, P(wq), P(ws), N, P(0), epi, P(y), P(wsp), nb, P(0))
+
+    assert call(K=96, ldx=96) == 1  # K % 64
+    assert call(nb=need - 1) == 1  # workspace too small
+    assert call(wsp=0) == 1 and call(x=0) == 1 and call(y=0) == 1
+    assert call(wsp=E + 16) == 1  # workspace not 256-byte aligned
+    assert call(ldx=60) == 1
+    assert call(wsp=A) == 1  # workspace overlaps x
+    assert call(y=B) == 1  # y overlaps the weights
+    assert call(N=264) == 2
+    assert call(M=0) == 0
 
 
 def test_forced_unsupported_path(L, monkeypatch):

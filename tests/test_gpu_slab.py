@@ -267,3 +267,22 @@ def test_ffn_chain_full_size_fused_requant():
     assert np.array_equal(hq, rq) and np.array_equal(hsc, rs)
     yref, S2 = oracle.linear_ref(rq, rs, *quant_ref(w2), bias=f64(b2))
     assert_linear_close(y[rows], yref, S2, what="ffn down after fused requant")
+
+
+@pytest.mark.parametrize("M,K,N,gelu", [(300, 512, 256, True), (77, 5120, 768, False)])
+def test_linear_ws_one_call(M, K, N, gelu):
+    # One call (quantize into the workspace, slab GEMM) equals the two calls
+    # bit for bit, with strided activation rows, and the oracle within tolerance.
+    d = dev()
+    base = synth.make_activation(M, K + 64, seed=M + K)
+    x = base[:, 32:32 + K]
+    w = synth.make_weight(N, K, seed=M + K)
+    b = synth.make_bias(N, seed=M + K)
+    wsl = mx().mx_quantize_weight_slab(w.to(d))
+    xd = base.to(d)[:, 32:32 + K]
+    y1 = mx().mx_linear_ws(xd, wsl, b.to(d), gelu=gelu)
+    y2 = mx().mx_linear_slab(mx().mx_quantize_act_slab(xd), wsl, b.to(d), gelu=gelu)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    yref, S = oracle_linear(x, w, b, gelu)
+    assert_linear_close(y1, yref, S, "gelu_tanh" if gelu else "none", what="linear_ws")
