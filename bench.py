@@ -23,7 +23,9 @@ Prints ONE JSON line. Besides the contract fields it carries
                 same inputs;
   extra         the activation quantizer's bandwidth, the same step on
                 row-major operands (mx_quantize_act + mx_linear_q), the
-                fused-prologue path (mx_linear), and the weight quantizer.
+                fused-prologue path (mx_linear), the weight quantizer, the
+                other Wan2.2 linears, and one whole denoise step's 400
+                linears (40 blocks) back to back.
 
 Modes for profiling: --profile step|rowmajor|fused runs only those kernels
 (steps times, no oracle); --profile-copy runs a 1 GiB device copy used to
@@ -188,6 +190,38 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
     return res
 
 
+def denoise_step(torch, synth, dev, steps=2, warmup=1):
+    """One full denoise step's quantized linears, back to back: 40 blocks x
+    10 linears (q|k|v and the text k|v fused, 7 GEMMs a block), each with its
+    own weights drawn on the GPU and quantized to slabs before timing, each
+    quantizing its input (the FFN intermediate in the up-projection's
+    epilogue)."""
+    from mxfp8_w8a8_quantized_amd.denoise import DenoiseStepLinears
+
+    step = DenoiseStepLinears(synth.DENOISE_BLOCKS, synth.VIDEO_TOKENS, synth.TEXT_TOKENS, synth.HIDDEN, synth.FFN, dev)
+    for block in range(synth.DENOISE_BLOCKS):
+        w, b = synth.make_denoise_block(block, dev, on_device=True)
+        step.set_block(block, w, b)
+        del w, b
+    inputs = synth.make_denoise_inputs(dev, on_device=True)
+    total, _ = timed_step(torch, [lambda: step.run(inputs)], steps, warmup)
+    ms = total / steps
+    flop = step.flop()
+    wbytes = sum(sl.q.numel() + sl.s.numel() for blk in step.weights for sl, _ in blk.values())
+    res = {
+        "blocks": step.blocks,
+        "linears": 10 * step.blocks,
+        "gemm_launches": len(step.shapes()) * step.blocks,
+        "weight_GiB": round(wbytes / 2**30, 3),
+        "ms": round(ms, 3),
+        "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
+        "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
+    }
+    del step, inputs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -331,6 +365,7 @@ def main():
     if not args.no_extra:
         del y
         out["extra"]["other_workloads"] = other_workloads(torch, mx, synth, dev)
+        out["extra"]["denoise_step"] = denoise_step(torch, synth, dev)
 
     if not args.no_cpu_baseline:
         del x, xsl, rowmajor

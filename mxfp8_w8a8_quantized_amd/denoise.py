@@ -1,0 +1,152 @@
+"""The quantized linears of one Wan2.2-A14B denoise step, run back to back.
+
+Model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)", section
+"Quantization Details": every transformer block carries ten MXFP8 W8A8
+linears (self-attention attn1 q, k, v, out; cross-attention attn2 q, k, v,
+out; the feed-forward ffn.net.0.proj with GELU-tanh and ffn.net.2), 40 blocks
+in all, each with its own E4M3 weights, E8M0 scales and F16 bias, and each
+quantizing its activation at run time.
+
+This module only arranges library calls; every value is computed by the HIP
+kernels behind the C ABI:
+
+* attn1 q, k and v read the same hidden states, so they run as one GEMM on
+  the row-concatenated weights (N = 3 * hidden); attn2 k and v likewise on the
+  text tokens (N = 2 * hidden). An output column depends only on its own weight
+  row, so the concatenation changes no value; the outputs are column blocks
+  of one bf16 tensor.
+* Each of those linears is one mx_linear_ws call: the activation is quantized
+  into the shared workspace slab, then multiplied by the slab weights.
+* The feed-forward pair quantizes its input into the workspace, runs
+  ffn.net.0.proj with the requantizing epilogue (the MX slab of its bf16 GELU
+  output, never written as bf16) and ffn.net.2 on that slab.
+
+The parts of a block that are not quantized linears (norms, modulation,
+attention itself, residual adds) are not here: the caller hands in the
+activation each linear reads, by input role (``ROLES``).
+"""
+
+import torch
+
+from . import Slab, mx_linear_slab, mx_linear_slab_requant, mx_linear_ws, mx_linear_ws_bytes
+from . import mx_quantize_act_slab, mx_quantize_weight_slab, mx_slab_rows
+
+# Input role of each GEMM of a block, in call order, with the linears it
+# fuses (names as in the Wan2.2 transformer's state dict).
+GEMMS = (
+    ("attn1.qkv", "attn1", ("attn1.to_q", "attn1.to_k", "attn1.to_v"), False),
+    ("attn1.to_out.0", "attn1.out", ("attn1.to_out.0",), False),
+    ("attn2.to_q", "attn2", ("attn2.to_q",), False),
+    ("attn2.kv", "text", ("attn2.to_k", "attn2.to_v"), False),
+    ("attn2.to_out.0", "attn2.out", ("attn2.to_out.0",), False),
+    ("ffn.net.0.proj", "ffn", ("ffn.net.0.proj",), True),
+    ("ffn.net.2", None, ("ffn.net.2",), False),
+)
+ROLES = ("attn1", "attn1.out", "attn2", "text", "attn2.out", "ffn")
+LINEARS = tuple(name for _, _, names, _ in GEMMS for name in names)
+
+
+class DenoiseStepLinears:
+    """Slab weights of `blocks` transformer blocks and the buffers to run
+    their 10 * blocks quantized linears on `tokens` video tokens and
+    `text_tokens` text tokens.
+
+    set_block() quantizes one block's weights; run_block() / run() enqueue the
+    linears on the current stream of `device`. Outputs (bf16, overwritten by
+    every block) are in ``outputs``, keyed by GEMM name; the feed-forward
+    intermediate stays an MX slab (``ffn_hidden``).
+    """
+
+    def __init__(self, blocks, tokens, text_tokens, hidden, ffn, device):
+        self.blocks, self.tokens, self.text_tokens = blocks, tokens, text_tokens
+        self.hidden, self.ffn, self.device = hidden, ffn, torch.device(device)
+        self.weights = [None] * blocks
+        self.rows = {"attn1": tokens, "attn1.out": tokens, "attn2": tokens, "text": text_tokens,
+                     "attn2.out": tokens, "ffn": tokens}
+        n_out = {"attn1.qkv": 3 * hidden, "attn1.to_out.0": hidden, "attn2.to_q": hidden,
+                 "attn2.kv": 2 * hidden, "attn2.to_out.0": hidden, "ffn.net.2": hidden}
+        self.outputs = {}
+        for gemm, role, _, _ in GEMMS:
+            if gemm in n_out:
+                M = tokens if role is None else self.rows[role]
+                self.outputs[gemm] = torch.empty((M, n_out[gemm]), dtype=torch.bfloat16, device=self.device)
+        self.ffn_hidden = Slab(
+            torch.empty((ffn // 64, mx_slab_rows(tokens), 64), dtype=torch.uint8, device=self.device),
+            torch.empty((ffn // 64, mx_slab_rows(tokens), 2), dtype=torch.uint8, device=self.device),
+            tokens,
+        )
+        ws = max(mx_linear_ws_bytes(tokens, hidden), mx_linear_ws_bytes(text_tokens, hidden))
+        if ws < 0:
+            raise ValueError("hidden must be a multiple of 64")
+        self.workspace = torch.empty((ws,), dtype=torch.uint8, device=self.device)
+        # The workspace viewed as the feed-forward input's slab, the layout
+        # mx_linear_ws gives it (codes, then scales).
+        R = mx_slab_rows(tokens)
+        nq = R * hidden
+        self.ffn_input = Slab(
+            self.workspace[:nq].view(hidden // 64, R, 64),
+            self.workspace[nq : nq + nq // 32].view(hidden // 64, R, 2),
+            tokens,
+        )
+
+    def shapes(self):
+        """(gemm name, M, K, N, gelu) of the GEMMs of one block, in call order."""
+        out = []
+        for gemm, role, names, gelu in GEMMS:
+            M = self.tokens if role is None else self.rows[role]
+            K = self.ffn if gemm == "ffn.net.2" else self.hidden
+            N = {"attn1.qkv": 3 * self.hidden, "attn2.kv": 2 * self.hidden, "ffn.net.0.proj": self.ffn}.get(
+                gemm, self.hidden)
+            out.append((gemm, M, K, N, gelu))
+        return out
+
+    def flop(self):
+        """Multiply-adds x 2 of one whole step (all blocks)."""
+        return self.blocks * sum(2.0 * M * K * N for _, M, K, N, _ in self.shapes())
+
+    def set_block(self, block, weights, biases):
+        """Quantize block `block`'s weights into slabs. weights: linear name ->
+        fp32 or bf16 [N, K] on the device (nn.Linear orientation); biases:
+        linear name -> f16 [N] on the device. The caller's tensors are not kept."""
+        if not 0 <= block < self.blocks:
+            raise IndexError(f"block {block} out of range [0, {self.blocks})")
+        missing = [n for n in LINEARS if n not in weights or n not in biases]
+        if missing:
+            raise KeyError(f"missing weights or biases for {missing}")
+        slabs = {}
+        for gemm, _, names, _ in GEMMS:
+            w = weights[names[0]] if len(names) == 1 else torch.cat([weights[n] for n in names], dim=0)
+            b = biases[names[0]] if len(names) == 1 else torch.cat([biases[n] for n in names], dim=0)
+            slabs[gemm] = (mx_quantize_weight_slab(w), b.contiguous())
+        self.weights[block] = slabs
+
+    def _check_inputs(self, inputs):
+        for role in ROLES:
+            x = inputs.get(role)
+            if x is None:
+                raise KeyError(f"missing input role {role!r}")
+            if x.device != self.device or x.dtype != torch.bfloat16 or tuple(x.shape) != (self.rows[role], self.hidden):
+                raise ValueError(f"input {role!r} must be bf16 [{self.rows[role]}, {self.hidden}] on {self.device}")
+
+    def run_block(self, block, inputs, check=True):
+        """Enqueue block `block`'s linears on the inputs (role -> bf16 tensor)."""
+        slabs = self.weights[block]
+        if slabs is None:
+            raise RuntimeError(f"block {block} has no weights (set_block)")
+        if check:
+            self._check_inputs(inputs)
+        for gemm, role, _, gelu in GEMMS:
+            w, b = slabs[gemm]
+            if gemm == "ffn.net.0.proj":
+                mx_quantize_act_slab(inputs[role], self.ffn_input)
+                mx_linear_slab_requant(self.ffn_input, w, b, gelu=gelu, out=self.ffn_hidden)
+            elif gemm == "ffn.net.2":
+                mx_linear_slab(self.ffn_hidden, w, b, gelu=gelu, y=self.outputs[gemm])
+            else:
+                mx_linear_ws(inputs[role], w, b, gelu=gelu, y=self.outputs[gemm], workspace=self.workspace)
+
+    def run(self, inputs):
+        """Enqueue the whole step: every block's linears, in block order."""
+        self._check_inputs(inputs)
+        for block in range(self.blocks):
+            self.run_block(block, inputs, check=False)

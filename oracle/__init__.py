@@ -12,6 +12,8 @@ definitions and the passages each function follows.
 from .mx_oracle import (  # noqa: F401
     E4M3_MAX,
     E4M3_EMAX,
+    E8M0_BIAS,
+    GELU_SLOPE_MAX,
     GROUP,
     bf16_round,
     bf16_ulp,

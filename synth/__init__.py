@@ -23,6 +23,9 @@ are zero (padding).
 
 from .inputs import (  # noqa: F401
     CONFIGS,
+    DENOISE_BLOCKS,
+    DENOISE_LINEARS,
+    DENOISE_ROLE_SEEDS,
     HIDDEN,
     FFN,
     TEXT_TOKENS,
@@ -32,6 +35,8 @@ from .inputs import (  # noqa: F401
     make_activation,
     make_activation_device,
     make_bias,
+    make_denoise_block,
+    make_denoise_inputs,
     make_text_context,
     make_weight,
     make_weight_device,

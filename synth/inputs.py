@@ -126,3 +126,59 @@ CONFIGS = {
         LinearShape("attn2.out", VIDEO_TOKENS, HIDDEN, HIDDEN),
     ],
 }
+
+
+# One denoise step: the ten quantized linears of each transformer block, in
+# call order (slot i of block b draws its weight and bias from
+# block_layer_seed(b, i)). Each linear reads the activation of one input
+# role; the roles stand in for the tensors the unquantized parts of the block
+# (norms, attention, residual adds) would hand over, so every video-side role
+# is a bf16 [VIDEO_TOKENS, HIDDEN] activation of the usual recipe and the text
+# role is the padded text context. ffn.net.2 reads the requantized output of
+# ffn.net.0.proj instead of a role.
+DENOISE_BLOCKS = 40
+DENOISE_LINEARS = (
+    (LinearShape("attn1.to_q", VIDEO_TOKENS, HIDDEN, HIDDEN), "attn1"),
+    (LinearShape("attn1.to_k", VIDEO_TOKENS, HIDDEN, HIDDEN), "attn1"),
+    (LinearShape("attn1.to_v", VIDEO_TOKENS, HIDDEN, HIDDEN), "attn1"),
+    (LinearShape("attn1.to_out.0", VIDEO_TOKENS, HIDDEN, HIDDEN), "attn1.out"),
+    (LinearShape("attn2.to_q", VIDEO_TOKENS, HIDDEN, HIDDEN), "attn2"),
+    (LinearShape("attn2.to_k", TEXT_TOKENS, HIDDEN, HIDDEN), "text"),
+    (LinearShape("attn2.to_v", TEXT_TOKENS, HIDDEN, HIDDEN), "text"),
+    (LinearShape("attn2.to_out.0", VIDEO_TOKENS, HIDDEN, HIDDEN), "attn2.out"),
+    (LinearShape("ffn.net.0.proj", VIDEO_TOKENS, HIDDEN, FFN, gelu=True), "ffn"),
+    (LinearShape("ffn.net.2", VIDEO_TOKENS, FFN, HIDDEN), None),
+)
+DENOISE_ROLE_SEEDS = {"attn1": 101, "attn1.out": 102, "attn2": 103, "attn2.out": 104, "ffn": 105, "text": 106}
+
+
+def make_denoise_inputs(device=None, on_device=False):
+    """The activation of every input role of the denoise step (see
+    DENOISE_LINEARS), seeded by DENOISE_ROLE_SEEDS. Drawn on the host and
+    moved to `device`, or with on_device=True drawn there directly."""
+    out = {}
+    for role, seed in DENOISE_ROLE_SEEDS.items():
+        if role == "text":
+            x = make_text_context(TEXT_TOKENS, HIDDEN, seed)
+        elif on_device:
+            x = make_activation_device(VIDEO_TOKENS, HIDDEN, seed, device)
+        else:
+            x = make_activation(VIDEO_TOKENS, HIDDEN, seed)
+        out[role] = x.to(device) if device is not None else x
+    return out
+
+
+def make_denoise_block(block, device=None, on_device=False):
+    """Weights (fp32 [N, K]) and f16 biases of the ten linears of one block,
+    keyed by linear name; on_device=True draws the weights on `device`."""
+    weights, biases = {}, {}
+    for slot, (shp, _) in enumerate(DENOISE_LINEARS):
+        seed = block_layer_seed(block, slot)
+        if on_device:
+            w = make_weight_device(shp.N, shp.K, seed, device)
+        else:
+            w = make_weight(shp.N, shp.K, seed)
+        b = make_bias(shp.N, seed)
+        weights[shp.name] = w.to(device) if device is not None else w
+        biases[shp.name] = b.to(device) if device is not None else b
+    return weights, biases

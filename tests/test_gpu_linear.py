@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_linear_close, dev, f64, mx, quant_ref, u8
+from helpers import assert_chain_close, assert_linear_close, dev, f64, mx, quant_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +34,12 @@ def run_case(M, K, N, seed, bias=True, gelu=False, fused=True, x=None):
     return x, w, b, wq, ws, y
 
 
-def oracle_linear(x, wq, ws, b, gelu):
+def oracle_linear(x, w, b, gelu, wref=None):
+    """The oracle's linear on the seeded inputs (wref: the oracle's codes and
+    scales of w, when the caller has them already)."""
     xq, xs = quant_ref(x)
-    return oracle.linear_ref(xq, xs, u8(wq), u8(ws), bias=None if b is None else f64(b),
+    wq, ws = quant_ref(w) if wref is None else wref
+    return oracle.linear_ref(xq, xs, wq, ws, bias=None if b is None else f64(b),
                              epilogue="gelu_tanh" if gelu else "none")
 
 
@@ -48,14 +51,14 @@ def oracle_linear(x, wq, ws, b, gelu):
 def test_linear_small_shapes(M, K, N, fused):
     print(f"linear M={M} K={K} N={N} fused={fused}", flush=True)
     x, w, b, wq, ws, y = run_case(M, K, N, seed=M * 7 + K + N, fused=fused)
-    yref, S = oracle_linear(x, wq, ws, b, False)
+    yref, S = oracle_linear(x, w, b, False)
     assert_linear_close(y, yref, S, what=f"M{M} K{K} N{N}")
 
 
 @pytest.mark.parametrize("fused", [True, False])
 def test_linear_gelu_no_bias(fused):
     x, w, b, wq, ws, y = run_case(300, 256, 512, seed=5, bias=False, gelu=True, fused=fused)
-    yref, S = oracle_linear(x, wq, ws, None, True)
+    yref, S = oracle_linear(x, w, None, True)
     assert_linear_close(y, yref, S, "gelu_tanh", what="gelu")
 
 
@@ -100,7 +103,7 @@ def test_zero_rows_give_bias():
     yg = f64(y)
     want = f64(b.float().to(torch.bfloat16))  # bf16(f32(bias))
     assert np.array_equal(yg[410:], np.broadcast_to(want, (102, 1024)))
-    yref, S = oracle_linear(x, wq, ws, b, False)
+    yref, S = oracle_linear(x, w, b, False)
     assert_linear_close(y, yref, S, what="text ctx")
 
 
@@ -146,15 +149,16 @@ def test_workload_configs(cfg):
         y = mx().mx_linear(xd, wq, ws, b.to(d), gelu=shp.gelu)
         torch.cuda.synchronize()
         rows = np.arange(shp.M) if shp.M <= 512 else sampled_rows(shp.M)
-        yref, S = oracle_linear(x[rows], wq, ws, b, shp.gelu)
+        yref, S = oracle_linear(x[rows], w, b, shp.gelu)
         assert_linear_close(y[rows], yref, S, "gelu_tanh" if shp.gelu else "none", what=f"{cfg}/{shp.name}")
         del y, xd
 
 
 def test_ffn_chain_requantizes_intermediate():
     # ffn.net.0.proj (GELU) then ffn.net.2 on the bf16 intermediate h, which
-    # the second call quantizes on the fly. The down-projection is checked
-    # against the oracle on the quantization of the GPU's own h.
+    # the second call quantizes on the fly. h is held to the oracle's first
+    # linear; the down-projection to the oracle's whole chain from the seeded
+    # inputs (assert_chain_close).
     d = dev()
     up, down = synth.CONFIGS["ffn_75348x5120x13824"]
     M = 2048 + 84  # several token tiles and the same ragged tail as 75348
@@ -167,7 +171,6 @@ def test_ffn_chain_requantizes_intermediate():
     y = mx().mx_linear(h, w2q, w2s, b2.to(d))
     torch.cuda.synchronize()
     rows = sampled_rows(M, 64, seed=1)
-    href, S1 = oracle_linear(x[rows], w1q, w1s, b1, True)
+    href, S1 = oracle_linear(x[rows], w1, b1, True)
     assert_linear_close(h[rows], href, S1, "gelu_tanh", what="ffn up")
-    yref, S2 = oracle_linear(h[rows].cpu(), w2q, w2s, b2, False)
-    assert_linear_close(y[rows], yref, S2, what="ffn down")
+    assert_chain_close(y[rows], href, S1, "gelu_tanh", *quant_ref(w2), f64(b2), what="ffn down")

@@ -19,7 +19,17 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_linear_close, dev, f64, mx, quant_ref, u8
+from helpers import (
+    assert_chain_close,
+    assert_linear_close,
+    assert_requant_valid,
+    dev,
+    f64,
+    mx,
+    quant_ref,
+    requant_range,
+    u8,
+)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,15 +200,16 @@ def test_linear_slab_qkv_full_size():
     assert torch.equal(y.view(torch.int16), y_rm.view(torch.int16))
     del y_rm, xq, xsr
     rows = sampled_rows(shp.M)
-    yref, S = oracle.linear_ref(*quant_ref(x[rows]), u8(wq), u8(wsr), bias=f64(b))
+    yref, S = oracle.linear_ref(*quant_ref(x[rows]), *quant_ref(w), bias=f64(b))
     assert_linear_close(y[rows], yref, S, what="qkv slab")
 
 
 def test_ffn_chain_full_size_slab():
     # ffn.net.0.proj (GELU) then ffn.net.2 over all 75348 tokens: the bf16
     # intermediate h [75348, 13824] is quantized again into a slab of 216
-    # K-slabs (offsets past 2^30 bytes). Down-projection rows are checked
-    # against the oracle on the quantization of the GPU's own h.
+    # K-slabs (offsets past 2^30 bytes). h is held to the oracle's first
+    # linear, its slab to what the oracle's chain fixes of it, and the
+    # down-projection to the oracle's whole chain (assert_chain_close).
     d = dev()
     up, down = synth.CONFIGS["ffn_75348x5120x13824"]
     print(f"slab ffn {up} -> {down}", flush=True)
@@ -212,13 +223,11 @@ def test_ffn_chain_full_size_slab():
     y = mx().mx_linear_slab(hs, w2s, b2.to(d))
     torch.cuda.synchronize()
     rows = sampled_rows(up.M, 48, seed=3)
-    hq, hsc = slab_rows_of(hs, torch.from_numpy(rows))
-    rq, rs = quant_ref(h[rows])
-    assert np.array_equal(hsc, rs) and np.array_equal(hq, rq)
     href, S1 = oracle_linear(x[rows], w1, b1, True)
     assert_linear_close(h[rows], href, S1, "gelu_tanh", what="ffn up")
-    yref, S2 = oracle.linear_ref(rq, rs, *quant_ref(w2), bias=f64(b2))
-    assert_linear_close(y[rows], yref, S2, what="ffn down")
+    assert_requant_valid(*slab_rows_of(hs, torch.from_numpy(rows)), requant_range(href, S1, "gelu_tanh"),
+                         what="ffn intermediate slab")
+    assert_chain_close(y[rows], href, S1, "gelu_tanh", *quant_ref(w2), f64(b2), what="ffn down")
 
 
 @pytest.mark.parametrize("M,K,N,gelu", [(300, 256, 320, True), (513, 512, 256, False), (70, 5120, 768, True), (1, 64, 64, True)])
@@ -236,15 +245,17 @@ def test_requant_epilogue_equals_two_pass(M, K, N, gelu):
     torch.cuda.synchronize()
     assert torch.equal(out.q, ref.q) and torch.equal(out.s, ref.s)
     assert not out.q[:, M:].any() and not out.s[:, M:].any()
-    # and against the oracle's quantization of the same bf16 values
-    rq, rs = to_slab(*quant_ref(y))
-    assert np.array_equal(u8(out.q), rq) and np.array_equal(u8(out.s), rs)
+    # and against what the oracle's linear fixes of the requantized output
+    yref, S = oracle_linear(synth.make_activation(M, K, seed=M + N), synth.make_weight(N, K, seed=M + N),
+                            synth.make_bias(N, seed=M + N), gelu)
+    assert_requant_valid(*slab_rows_of(out, torch.arange(M)), requant_range(yref, S, "gelu_tanh" if gelu else "none"),
+                         what="requantized output")
 
 
 def test_ffn_chain_full_size_fused_requant():
     # ffn.net.0.proj with GELU writing the requantized intermediate directly,
     # then ffn.net.2: bit-identical to the two-pass chain, and sampled rows
-    # against the oracle.
+    # against the oracle's chain from the seeded inputs.
     d = dev()
     up, down = synth.CONFIGS["ffn_75348x5120x13824"]
     print(f"slab ffn fused requant {up} -> {down}", flush=True)
@@ -262,11 +273,11 @@ def test_ffn_chain_full_size_fused_requant():
     assert torch.equal(hs.q, hs2.q) and torch.equal(hs.s, hs2.s)
     del hs2
     rows = sampled_rows(up.M, 48, seed=5)
-    rq, rs = quant_ref(h[rows])
-    hq, hsc = slab_rows_of(hs, torch.from_numpy(rows))
-    assert np.array_equal(hq, rq) and np.array_equal(hsc, rs)
-    yref, S2 = oracle.linear_ref(rq, rs, *quant_ref(w2), bias=f64(b2))
-    assert_linear_close(y[rows], yref, S2, what="ffn down after fused requant")
+    href, S1 = oracle_linear(x[rows], w1, b1, True)
+    assert_linear_close(h[rows], href, S1, "gelu_tanh", what="ffn up")
+    assert_requant_valid(*slab_rows_of(hs, torch.from_numpy(rows)), requant_range(href, S1, "gelu_tanh"),
+                         what="ffn intermediate slab")
+    assert_chain_close(y[rows], href, S1, "gelu_tanh", *quant_ref(w2), f64(b2), what="ffn down after fused requant")
 
 
 @pytest.mark.parametrize("M,K,N,gelu", [(300, 512, 256, True), (77, 5120, 768, False)])

@@ -64,3 +64,33 @@ def test_workload_shapes():
     for shapes in c.values():
         for s in shapes:
             assert s.K % 32 == 0
+
+
+def test_denoise_step_table():
+    # Ten quantized linears per block, 40 blocks, as the model card lists
+    # them; about 14 GiB of E4M3 codes + E8M0 scales in all.
+    lin = synth.DENOISE_LINEARS
+    assert synth.DENOISE_BLOCKS == 40 and len(lin) == 10
+    assert [s.name for s, _ in lin] == [
+        "attn1.to_q", "attn1.to_k", "attn1.to_v", "attn1.to_out.0",
+        "attn2.to_q", "attn2.to_k", "attn2.to_v", "attn2.to_out.0",
+        "ffn.net.0.proj", "ffn.net.2",
+    ]
+    assert {r for _, r in lin if r} == set(synth.DENOISE_ROLE_SEEDS)
+    n_param = sum(s.N * s.K for s, _ in lin) * synth.DENOISE_BLOCKS
+    gib = n_param * (1 + 1 / 32) / 2**30
+    assert 13.0 < gib < 14.0
+    flop = 2 * sum(s.M * s.N * s.K for s, _ in lin) * synth.DENOISE_BLOCKS
+    assert abs(flop / 1.8035e15 - 1) < 1e-3
+    seeds = {synth.block_layer_seed(b, i) for b in range(40) for i in range(10)}
+    assert len(seeds) == 400
+
+
+def test_denoise_block_weights_are_seeded_per_slot():
+    w0, b0 = synth.make_denoise_block(0)
+    w0b, _ = synth.make_denoise_block(0)
+    assert all(torch.equal(w0[k], w0b[k]) for k in w0)
+    w1, _ = synth.make_denoise_block(1)
+    assert not torch.equal(w0["attn1.to_q"], w1["attn1.to_q"])
+    assert not torch.equal(w0["attn1.to_q"][:16], w0["attn1.to_k"][:16])
+    assert w0["ffn.net.2"].shape == (5120, 13824) and b0["ffn.net.0.proj"].dtype == torch.float16
