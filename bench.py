@@ -96,6 +96,34 @@ def timed_step(torch, fns, steps, warmup):
     return start.elapsed_time(end), per
 
 
+def graph_ms(torch, fn, reps, per_graph=5):
+    """ms per call of fn replayed from a captured HIP graph (per_graph calls
+    per graph), i.e. without the host's launch cost: what a serving loop
+    that captures its launches would see."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * per_graph)
+    del g
+    return ms
+
+
 def mean(v):
     return sum(v) / len(v)
 
@@ -153,22 +181,35 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
                 x = synth.make_activation_device(shp.M, shp.K, 500 + li, dev)
             acts.append(x)
         outs = [torch.empty((shp.M, shp.N), dtype=torch.bfloat16, device=dev) for shp, _, _ in layers]
-        slabs = [None] * len(layers)
+        slabs = [mx.mx_quantize_act_slab(acts[li] if acts[li] is not None else outs[li - 1])
+                 for li in range(len(layers))]
+        # Few token tiles: split-K (partial sums in a workspace, ordered reduction).
+        splits = [mx.mx_linear_splitk_choose(shp.M, shp.K, shp.N) for shp, _, _ in layers]
+        wss = [torch.empty((mx.mx_linear_splitk_ws_bytes(shp.M, shp.N, sp),), dtype=torch.uint8, device=dev)
+               if sp > 1 else None for (shp, _, _), sp in zip(layers, splits)]
 
         def run():
             for li, (shp, w, b) in enumerate(layers):
                 x = acts[li] if acts[li] is not None else outs[li - 1]
-                slabs[li] = mx.mx_quantize_act_slab(x, slabs[li])
-                mx.mx_linear_slab(slabs[li], w, b, gelu=shp.gelu, y=outs[li])
+                mx.mx_quantize_act_slab(x, slabs[li])
+                if splits[li] > 1:
+                    mx.mx_linear_slab_splitk(slabs[li], w, b, gelu=shp.gelu, y=outs[li], splits=splits[li],
+                                             workspace=wss[li])
+                else:
+                    mx.mx_linear_slab(slabs[li], w, b, gelu=shp.gelu, y=outs[li])
 
         total, _ = timed_step(torch, [run], steps, warmup)
         ms = total / steps
+        g_ms = graph_ms(torch, run, steps)
         flop = sum(2.0 * shp.M * shp.N * shp.K for shp, _, _ in layers)
         res[name] = {
-            "linears": [f"{shp.name} {shp.M}x{shp.K}x{shp.N}" + (" gelu" if shp.gelu else "") for shp, _, _ in layers],
+            "linears": [f"{shp.name} {shp.M}x{shp.K}x{shp.N}" + (" gelu" if shp.gelu else "")
+                        + (f" splitk{sp}" if sp > 1 else "") for (shp, _, _), sp in zip(layers, splits)],
             "ms": round(ms, 4),
             "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
             "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
+            "graph_ms": round(g_ms, 4),
+            "graph_TFLOPs": round(flop / (g_ms * 1e-3) / 1e12, 2),
         }
         if [shp.name for shp, _, _ in layers] == ["ffn.net.0.proj", "ffn.net.2"]:
             # The same pair with the requantization fused into the up-projection.

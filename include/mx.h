@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 4
+#define MX_ABI_VERSION 5
 
 typedef enum {
   MX_OK = 0,
@@ -185,6 +185,38 @@ int mx_linear_ws(const void* x, int64_t M, int64_t K, int64_t ldx,
                  const uint8_t* wq, const uint8_t* ws, int64_t N,
                  const void* bias, int epilogue, void* y,
                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Split-K for few token tiles. With M of a few hundred tokens (the 128-token
+ * linear, the 512 text tokens of attn2 k/v) the 256 x 256 tiles are too few to
+ * occupy the GPU's CUs, and each one runs the whole K loop. The split-K form
+ * gives each tile `splits` consecutive ranges of the K/64 slabs, one
+ * workgroup per (tile, range), writing fp32 partial sums into a workspace;
+ * a second kernel adds the ranges in order 0, 1, ..., adds the bias, applies
+ * the epilogue and rounds to bf16. The reduction order is fixed, so results
+ * are deterministic; with splits = 1 they equal mx_linear_slab bit for bit,
+ * otherwise the fp32 sums are associated differently (same tolerance).
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for mx_linear_slab_splitk: splits * T * 256 KiB with
+ * T = ceil(M/256) * ceil(N/256) (fp32 partial tiles); -1 on bad arguments. */
+int64_t mx_linear_splitk_ws_bytes(int64_t M, int64_t N, int splits);
+
+/* A split count that gives at most one workgroup per CU of an MI355X (256),
+ * at most 8 ranges (the partial sums' traffic grows with the count) and at
+ * least two 64-K slabs per range; 1 when the tiles alone fill the CUs. */
+int mx_linear_splitk_choose(int64_t M, int64_t K, int64_t N);
+
+/* mx_linear_slab with split-K (operands, bias, epilogue and y as there).
+ * 1 <= splits <= K/64 (else MX_ERR_INVALID_ARGUMENT); T * splits <= 2^24
+ * (else MX_ERR_UNSUPPORTED). workspace: device memory of at least
+ * mx_linear_splitk_ws_bytes(M, N, splits) bytes, 256-byte aligned, not
+ * overlapping the operands, bias or y; overwritten. Two kernels on `stream`;
+ * nothing is allocated. */
+int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                          const uint8_t* wq, const uint8_t* ws, int64_t N,
+                          const void* bias, int epilogue, void* y, int splits,
+                          void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,9 @@ SIGNATURES = {
     "mx_linear_slab_requant": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _P], _INT),
     "mx_linear_ws_bytes": ([_I64, _I64], _I64),
     "mx_linear_ws": ([_P, _I64, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
+    "mx_linear_splitk_ws_bytes": ([_I64, _I64, _INT], _I64),
+    "mx_linear_splitk_choose": ([_I64, _I64, _I64], _INT),
+    "mx_linear_slab_splitk": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
 }
 
 
@@ -369,6 +372,39 @@ def mx_linear_ws(x, w, bias=None, gelu=False, y=None, workspace=None):
             lib().mx_linear_ws(
                 _ptr(x), M, K, ld, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _ptr(workspace),
                 workspace.numel(), _stream(dev),
+            )
+        )
+    return y
+
+
+def mx_linear_splitk_ws_bytes(M, N, splits):
+    return lib().mx_linear_splitk_ws_bytes(M, N, splits)
+
+
+def mx_linear_splitk_choose(M, K, N):
+    return lib().mx_linear_splitk_choose(M, K, N)
+
+
+def mx_linear_slab_splitk(x, w, bias=None, gelu=False, y=None, splits=None, workspace=None):
+    """mx_linear_slab with split-K over `splits` K ranges (default
+    mx_linear_splitk_choose); workspace: uint8 of at least
+    mx_linear_splitk_ws_bytes(M, N, splits) bytes (allocated here when None)."""
+    dev, M, N, K = _slab_linear_args(x, w, bias)
+    splits = mx_linear_splitk_choose(M, K, N) if splits is None else int(splits)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    if workspace is None:
+        need = mx_linear_splitk_ws_bytes(M, N, splits)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_slab_splitk(
+                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), splits,
+                _ptr(workspace), workspace.numel(), _stream(dev),
             )
         )
     return y

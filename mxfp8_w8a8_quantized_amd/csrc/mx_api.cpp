@@ -3,6 +3,7 @@
 // any HIP call, so the error paths need no GPU.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdint>
@@ -42,6 +43,9 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
 
 constexpr int64_t kMaxKN = int64_t(1) << 20;   // keeps in-tile byte offsets below 2^30
 constexpr int64_t kMaxRows = int64_t(1) << 30;
+constexpr int64_t kSplitTargetWorkgroups = 256;  // one workgroup per CU of an MI355X
+constexpr int64_t kMaxSplitWorkgroups = int64_t(1) << 24;
+constexpr int64_t kMaxAutoSplits = 8;  // 128 x 5120 x 5120: 8 splits 19.5 us, 12 splits 20.7 us
 
 int check_k(int64_t K) {
   if (K <= 0 || K % 32 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a positive multiple of 32", (long long)K);
@@ -333,6 +337,51 @@ int mx_linear_ws(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t
   hipError_t e = mx::launch_quantize_slab(0, x, M, K, ldx, xq, xs, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return finish(mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
+                "linear launch");
+}
+
+int64_t mx_linear_splitk_ws_bytes(int64_t M, int64_t N, int splits) {
+  if (M < 0 || N < 0 || M > kMaxRows || N > kMaxKN || splits < 1 || splits > kMaxKN / 64) return -1;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return (int64_t)splits * tiles * 65536 * 4;
+}
+
+int mx_linear_splitk_choose(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || N <= 0 || K < 64 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN) return 1;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t nh = K / 64;
+  int64_t s = kSplitTargetWorkgroups / tiles;  // fill the CUs once, without a second partial round
+  s = std::min<int64_t>(s, kMaxAutoSplits);    // partial-sum traffic grows with the split count
+  s = std::min<int64_t>(s, nh / 2);            // at least two half-steps per range
+  return (int)std::max<int64_t>(s, 1);
+}
+
+int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                          const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y, int splits,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK) return st;
+  if (splits < 1 || splits > K / 64)
+    return fail(MX_ERR_INVALID_ARGUMENT, "splits = %d must be in [1, K/64 = %lld]", splits, (long long)(K / 64));
+  if (M == 0 || N == 0) return MX_OK;
+  if (y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL y or workspace");
+  if (!aligned(y, 16) || !aligned(workspace, 256))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned, workspace 256-byte aligned");
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles * splits > kMaxSplitWorkgroups)
+    return fail(MX_ERR_UNSUPPORTED, "%lld tiles x %d splits exceed 2^24 workgroups", (long long)tiles, splits);
+  const int64_t need = mx_linear_splitk_ws_bytes(M, N, splits);
+  if (workspace_bytes < need)
+    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+  const uint64_t ybytes = (uint64_t)M * N * 2;
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, y, ybytes, "y")) != MX_OK) return st;
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, workspace, (uint64_t)need, "workspace")) != MX_OK)
+    return st;
+  if (overlap(workspace, (uint64_t)need, y, ybytes)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps y");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear_slab_splitk(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, (float*)workspace,
+                                              (hipStream_t)stream),
                 "linear launch");
 }
 

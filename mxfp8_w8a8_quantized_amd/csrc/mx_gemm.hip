@@ -64,6 +64,8 @@ struct Params {
   uint16_t* y;           // bf16 bits
   uint8_t* hq;           // requantized output: codes slab [N/64][RM][64] (or null)
   uint8_t* hs;           //                     scales slab [N/64][RM][2]
+  float* part;           // split-K partial sums (or null), see slab::store_tile_part
+  int splits;            // K ranges per tile (split-K), else 1
   int M, N, K;
   int tiles_m, tiles_n;
 };
@@ -868,11 +870,47 @@ __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Pa
   }
 }
 
-template <int EPI, bool QOUT>
+// Split-K output: the wave's fp32 accumulators as they sit in registers,
+// for mx_linear_slab_splitk's reduction. Partial tile (ks, tile) holds 65536
+// floats; 16-byte chunk c = (((wave * 4 + i) * 4 + j) * 4 + q) * 64 + lane is
+// acc[i][j][4q .. 4q+3] of that lane: token m = m0 + 128 wm + 32 j + lane%32,
+// weight rows n = n0 + 128 wn + 32 i + 8 q + 4 (lane/32) + 0..3. One store
+// instruction writes 1 KB of consecutive bytes. Chunks of tokens past M are
+// not written (the reduction skips them).
+__device__ __forceinline__ void store_tile_part(const f32x16 (&acc)[4][4], const Params& p, int tile, int ks, int m0,
+                                                int wave, int wm, int lane) {
+  float* base = p.part + ((size_t)ks * p.tiles_m * p.tiles_n + tile) * 65536;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(base, 65536u * 4u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = m0 + wm * 128 + 32 * j + (lane & 31) < p.M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int chunk = (((wave * 4 + i) * 4 + j) * 4 + q) * 64 + lane;
+        // Copy the elements out first: a bit_cast of a vector-element lvalue
+        // reads from the start of the vector (element 0) in this compiler.
+        const f32x4 f = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        const i32x4 v = __builtin_bit_cast(i32x4, f);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rp, ok ? chunk * 16 : kDropOffset, 0, 0);
+      }
+    }
+  }
+}
+
+enum { OUT_Y = 0, OUT_Q = 1, OUT_PART = 2 };
+
+template <int EPI, int OUT>
 __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
-  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  int bid = blockIdx.x, ks = 0;
+  if constexpr (OUT == OUT_PART) {
+    ks = bid % p.splits;
+    bid /= p.splits;
+  }
+  tile_coords(bid, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_m = min(p.M - m0, BM);
   const int rows_n = min(p.N - n0, BN);
@@ -880,14 +918,21 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
 
+  // K range of this workgroup: all K/64 half-steps, or split-K range ks.
+  int h0 = 0, nh_wg = p.K >> 6;
+  if constexpr (OUT == OUT_PART) {
+    const int tot = nh_wg;
+    h0 = ks * tot / p.splits;
+    nh_wg = (ks + 1) * tot / p.splits - h0;
+  }
   Src S;
   S.w_slab = (uint64_t)p.tiles_n * BN * 64;
   S.x_slab = (uint64_t)p.tiles_m * BM * 64;
-  S.w = p.wq + (size_t)n0 * 64;
-  S.x = p.x + (size_t)m0 * 64;
-  S.ws = p.ws + (size_t)n0 * 2;
-  S.xs = p.xs + (size_t)m0 * 2;
-  S.nh = p.K >> 6;
+  S.w = p.wq + (size_t)n0 * 64 + h0 * S.w_slab;
+  S.x = p.x + (size_t)m0 * 64 + h0 * S.x_slab;
+  S.ws = p.ws + (size_t)n0 * 2 + h0 * (S.w_slab >> 5);
+  S.xs = p.xs + (size_t)m0 * 2 + h0 * (S.x_slab >> 5);
+  S.nh = nh_wg;
   S.voff = (lane >> 2) * 64 + (((lane & 3) ^ (lane >> 4)) << 4);
 
   f32x16 acc[4][4];
@@ -916,16 +961,56 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  if constexpr (QOUT)
+  if constexpr (OUT == OUT_Q)
     store_tile_q<EPI>(acc, p, smem + wave * 32768, m0, n0, rows_n, wn, wm, lane);
+  else if constexpr (OUT == OUT_PART)
+    store_tile_part(acc, p, tm * p.tiles_n + tn, ks, m0, wave, wm, lane);
   else
     pp::store_tile8<EPI, 4>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
 
-template <int EPI, bool QOUT = false>
+// Split-K reduction: one thread per 16-byte chunk of the partial tiles (the
+// layout of store_tile_part), summing the splits in order 0, 1, ... (so the
+// result does not depend on timing), then bias, epilogue and bf16 as the
+// other kernels' epilogues do; 8 bytes of y per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(Params p) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  if (u >= tiles * 16384) return;
+  const int lane = (int)(u & 63), q = (int)(u >> 6) & 3, j = (int)(u >> 8) & 3, i = (int)(u >> 10) & 3;
+  const int wave = (int)(u >> 12) & 3;
+  const int tile = (int)(u >> 14);
+  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  const int m = tm * BM + (wave >> 1) * 128 + 32 * j + (lane & 31);
+  const int n = tn * BN + (wave & 1) * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
+  if (m >= p.M || n >= p.N) return;
+  const float* src = p.part + (size_t)tile * 65536 + (size_t)(u & 16383) * 4;
+  f32x4 s = *(const f32x4*)src;
+  for (int k = 1; k < p.splits; ++k) {
+    const f32x4 v = *(const f32x4*)(src + (size_t)k * tiles * 65536);
+    s[0] += v[0];
+    s[1] += v[1];
+    s[2] += v[2];
+    s[3] += v[3];
+  }
+  float b[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.bias != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, p.bias[n + r]);
+  }
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(s[r] + b[r]);
+  const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
+  const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
+  *(i32x2*)(p.y + (size_t)m * p.N + n) = i32x2{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1)};
+}
+
+template <int EPI, int OUT = OUT_Y>
 hipError_t launch(const Params& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
-  auto kern = linear_slab_kernel<EPI, QOUT>;
+  auto kern = linear_slab_kernel<EPI, OUT>;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
@@ -971,6 +1056,8 @@ hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
   p.y = (uint16_t*)y;
   p.hq = nullptr;
   p.hs = nullptr;
+  p.part = nullptr;
+  p.splits = 1;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -995,6 +1082,8 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
   p.y = (uint16_t*)y;
   p.hq = nullptr;
   p.hs = nullptr;
+  p.part = nullptr;
+  p.splits = 1;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -1016,13 +1105,45 @@ hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int6
   p.y = nullptr;
   p.hq = hq;
   p.hs = hs;
+  p.part = nullptr;
+  p.splits = 1;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
   p.tiles_m = (int)((M + BM - 1) / BM);
   p.tiles_n = (int)((N + BN - 1) / BN);
   const int nwg = p.tiles_m * p.tiles_n;
-  return epi == 1 ? slab::launch<1, true>(p, nwg, stream) : slab::launch<0, true>(p, nwg, stream);
+  return epi == 1 ? slab::launch<1, slab::OUT_Q>(p, nwg, stream) : slab::launch<0, slab::OUT_Q>(p, nwg, stream);
+}
+
+hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                     const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
+                                     float* part, hipStream_t stream) {
+  Params p;
+  p.x = xq;
+  p.xs = xs;
+  p.wq = wq;
+  p.ws = ws;
+  p.bias = (const uint16_t*)bias;
+  p.y = (uint16_t*)y;
+  p.hq = nullptr;
+  p.hs = nullptr;
+  p.part = part;
+  p.splits = splits;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  hipError_t e = slab::launch<0, slab::OUT_PART>(p, (int)(tiles * splits), stream);
+  if (e != hipSuccess) return e;
+  const int nred = (int)((tiles * 16384 + 255) / 256);
+  if (epi == 1)
+    hipLaunchKernelGGL(slab::splitk_reduce_kernel<1>, dim3(nred), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(slab::splitk_reduce_kernel<0>, dim3(nred), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace mx

@@ -44,4 +44,13 @@ hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int6
                                       const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias,
                                       int epi, uint8_t* hq, uint8_t* hs, hipStream_t stream);
 
+// Split-K slab GEMM: each tile's K/64 half-steps in `splits` ranges, one
+// workgroup per (tile, range) writing fp32 partial sums into `part`
+// (splits * tiles * 65536 floats), then a reduction kernel summing the
+// ranges in order and applying bias, epilogue and bf16 into y [M][N].
+// 1 <= splits <= K/64.
+hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                     const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
+                                     float* part, hipStream_t stream);
+
 }  // namespace mx

@@ -16,7 +16,9 @@ kernels behind the C ABI:
   row, so the concatenation changes no value; the outputs are column blocks
   of one bf16 tensor.
 * Each of those linears is one mx_linear_ws call: the activation is quantized
-  into the shared workspace slab, then multiplied by the slab weights.
+  into the shared workspace slab, then multiplied by the slab weights. The
+  text-token GEMM (512 tokens: too few tiles to occupy the GPU) quantizes into
+  the same slab and runs split-K (mx_linear_slab_splitk).
 * The feed-forward pair quantizes its input into the workspace, runs
   ffn.net.0.proj with the requantizing epilogue (the MX slab of its bf16 GELU
   output, never written as bf16) and ffn.net.2 on that slab.
@@ -28,8 +30,9 @@ activation each linear reads, by input role (``ROLES``).
 
 import torch
 
-from . import Slab, mx_linear_slab, mx_linear_slab_requant, mx_linear_ws, mx_linear_ws_bytes
-from . import mx_quantize_act_slab, mx_quantize_weight_slab, mx_slab_rows
+from . import Slab, mx_linear_slab, mx_linear_slab_requant, mx_linear_slab_splitk, mx_linear_splitk_choose
+from . import mx_linear_splitk_ws_bytes, mx_linear_ws, mx_linear_ws_bytes, mx_quantize_act_slab
+from . import mx_quantize_weight_slab, mx_slab_rows
 
 # Input role of each GEMM of a block, in call order, with the linears it
 # fuses (names as in the Wan2.2 transformer's state dict).
@@ -79,14 +82,27 @@ class DenoiseStepLinears:
         if ws < 0:
             raise ValueError("hidden must be a multiple of 64")
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=self.device)
-        # The workspace viewed as the feed-forward input's slab, the layout
-        # mx_linear_ws gives it (codes, then scales).
-        R = mx_slab_rows(tokens)
-        nq = R * hidden
-        self.ffn_input = Slab(
-            self.workspace[:nq].view(hidden // 64, R, 64),
-            self.workspace[nq : nq + nq // 32].view(hidden // 64, R, 2),
-            tokens,
+        # The workspace viewed as an input slab, the layout mx_linear_ws gives
+        # it (codes, then scales): the feed-forward input, the text tokens.
+        self.ffn_input = self._slab_view(tokens)
+        self.text_input = self._slab_view(text_tokens)
+        # Split counts per GEMM (1: mx_linear_ws) and the partial-sum workspace.
+        self.splits = {}
+        part = 0
+        for gemm, M, K, N, _ in self.shapes():
+            sp = mx_linear_splitk_choose(M, K, N) if gemm not in ("ffn.net.0.proj", "ffn.net.2") else 1
+            self.splits[gemm] = sp
+            if sp > 1:
+                part = max(part, mx_linear_splitk_ws_bytes(M, N, sp))
+        self.partials = torch.empty((part,), dtype=torch.uint8, device=self.device) if part else None
+
+    def _slab_view(self, rows):
+        R = mx_slab_rows(rows)
+        nq = R * self.hidden
+        return Slab(
+            self.workspace[:nq].view(self.hidden // 64, R, 64),
+            self.workspace[nq : nq + nq // 32].view(self.hidden // 64, R, 2),
+            rows,
         )
 
     def shapes(self):
@@ -142,6 +158,11 @@ class DenoiseStepLinears:
                 mx_linear_slab_requant(self.ffn_input, w, b, gelu=gelu, out=self.ffn_hidden)
             elif gemm == "ffn.net.2":
                 mx_linear_slab(self.ffn_hidden, w, b, gelu=gelu, y=self.outputs[gemm])
+            elif self.splits[gemm] > 1:
+                xs = self.text_input if role == "text" else self._slab_view(self.rows[role])
+                mx_quantize_act_slab(inputs[role], xs)
+                mx_linear_slab_splitk(xs, w, b, gelu=gelu, y=self.outputs[gemm], splits=self.splits[gemm],
+                                      workspace=self.partials)
             else:
                 mx_linear_ws(inputs[role], w, b, gelu=gelu, y=self.outputs[gemm], workspace=self.workspace)
 

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 4
+    assert L.mx_abi_version() == 5
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -174,6 +174,40 @@ def test_linear_ws_rejects_bad_arguments(L):
     assert call(y=B) == 1  # y overlaps the weights
     assert call(N=264) == 2
     assert call(M=0) == 0
+
+
+def test_splitk_sizes_and_choice(L):
+    # fp32 partial tiles: splits * ceil(M/256) * ceil(N/256) * 256 KiB
+    assert L.mx_linear_splitk_ws_bytes(128, 5120, 12) == 12 * 20 * 65536 * 4
+    assert L.mx_linear_splitk_ws_bytes(0, 64, 1) == 0
+    assert L.mx_linear_splitk_ws_bytes(1, 16, 0) == -1 and L.mx_linear_splitk_ws_bytes(-1, 16, 1) == -1
+    # about one workgroup per CU, at least two K slabs per range
+    assert L.mx_linear_splitk_choose(128, 5120, 5120) == 8  # 20 tiles; capped at 8
+    assert L.mx_linear_splitk_choose(512, 5120, 10240) == 3  # 80 tiles
+    assert L.mx_linear_splitk_choose(75348, 5120, 15360) == 1
+    assert L.mx_linear_splitk_choose(1, 256, 256) == 2  # K/64 = 4 slabs: two per range
+    assert L.mx_linear_splitk_choose(1, 64, 256) == 1
+    assert L.mx_linear_splitk_choose(0, 64, 256) == 1
+
+
+def test_splitk_rejects_bad_arguments(L):
+    f = L.mx_linear_slab_splitk
+    need = L.mx_linear_splitk_ws_bytes(8, 256, 2)
+    E = 0x50000000
+
+    def call(xq=A, xs=B, M=8, K=256, wq=C, ws=C + (1 << 20), N=256, epi=0, y=D, splits=2, wsp=E, nb=need):
+        return f(P(xq), P(xs), M, K, P(wq), P(ws), N, P(0), epi, P(y), splits, P(wsp), nb, P(0))
+
+    assert call(splits=0) == 1 and call(splits=5) == 1  # outside [1, K/64]
+    assert call(K=96) == 1  # K % 64
+    assert call(nb=need - 1) == 1
+    assert call(wsp=0) == 1 and call(y=0) == 1 and call(xq=0) == 1
+    assert call(wsp=E + 16) == 1
+    assert call(wsp=A) == 1  # workspace overlaps the token codes
+    assert call(y=E) == 1  # y overlaps the workspace
+    assert call(epi=7) == 1
+    assert call(N=264) == 2
+    assert call(M=0) == 0 and call(N=0) == 0
 
 
 def test_forced_unsupported_path(L, monkeypatch):

@@ -297,3 +297,59 @@ def test_linear_ws_one_call(M, K, N, gelu):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     yref, S = oracle_linear(x, w, b, gelu)
     assert_linear_close(y1, yref, S, "gelu_tanh" if gelu else "none", what="linear_ws")
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 512, 512), (300, 320, 272), (1, 64, 16), (513, 256, 1024)])
+def test_splitk_single_range_equals_slab(M, K, N):
+    # One range: the same accumulation, reduction of one term, same epilogue.
+    d = dev()
+    xs = mx().mx_quantize_act_slab(synth.make_activation(M, K, seed=M + K).to(d))
+    ws = mx().mx_quantize_weight_slab(synth.make_weight(N, K, seed=M + K).to(d))
+    b = synth.make_bias(N, seed=M + K).to(d)
+    for gelu in (False, True):
+        y1 = mx().mx_linear_slab(xs, ws, b, gelu=gelu)
+        y2 = mx().mx_linear_slab_splitk(xs, ws, b, gelu=gelu, splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize(
+    "M,K,N,splits,gelu,bias",
+    [(128, 512, 512, 8, False, True), (300, 320, 272, 5, True, True), (1, 64, 16, 1, False, False),
+     (513, 256, 1024, 3, True, False), (77, 5120, 768, 80, False, True), (256, 1024, 256, 7, True, True)],
+)
+def test_splitk_matches_oracle(M, K, N, splits, gelu, bias):
+    print(f"splitk M={M} K={K} N={N} splits={splits}", flush=True)
+    d = dev()
+    x = synth.make_activation(M, K, seed=M * 3 + N)
+    w = synth.make_weight(N, K, seed=M * 3 + N)
+    b = synth.make_bias(N, seed=M * 3 + N) if bias else None
+    xs = mx().mx_quantize_act_slab(x.to(d))
+    ws = mx().mx_quantize_weight_slab(w.to(d))
+    bd = None if b is None else b.to(d)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=d)
+    mx().mx_linear_slab_splitk(xs, ws, bd, gelu=gelu, y=y, splits=splits)
+    y2 = mx().mx_linear_slab_splitk(xs, ws, bd, gelu=gelu, splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # fixed reduction order
+    yref, S = oracle_linear(x, w, b, gelu)
+    assert_linear_close(y, yref, S, "gelu_tanh" if gelu else "none", what=f"splitk {splits}")
+
+
+@pytest.mark.parametrize("cfg", ["single_128x5120x5120", "xattn_512x5120x10240"])
+def test_splitk_small_token_configs(cfg):
+    # The linears with few token tiles at their full sizes, with the chosen
+    # split count; every output element against the oracle.
+    d = dev()
+    shp = synth.CONFIGS[cfg][0]
+    assert shp.M <= 512
+    x = synth.make_text_context(shp.M, shp.K, 31) if shp.M == synth.TEXT_TOKENS else synth.make_activation(shp.M, shp.K, 31)
+    w, b = synth.make_weight(shp.N, shp.K, 31), synth.make_bias(shp.N, 31)
+    splits = mx().mx_linear_splitk_choose(shp.M, shp.K, shp.N)
+    print(f"splitk {cfg} {shp} splits={splits}", flush=True)
+    assert splits > 1
+    y = mx().mx_linear_slab_splitk(mx().mx_quantize_act_slab(x.to(d)), mx().mx_quantize_weight_slab(w.to(d)),
+                                   b.to(d), gelu=shp.gelu)
+    torch.cuda.synchronize()
+    yref, S = oracle_linear(x, w, b, shp.gelu)
+    assert_linear_close(y, yref, S, "gelu_tanh" if shp.gelu else "none", what=cfg)
