@@ -82,6 +82,29 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Bias of a lane's 32x32-MFMA accumulators: quad k = 4 i + q holds the f16
+// bits of n = n0 + 128 wn + 32 i + 8 q + 4 (lane / 32) + 0..3. The 16 quads
+// are loaded together (one memory round trip rather than one per quad, each
+// behind a branch) through a buffer resource: zero past N, or everywhere
+// without a bias.
+struct BiasQuads {
+  i32x2 v[16];
+};
+
+__device__ __forceinline__ void load_bias_quads(BiasQuads& B, const Params& p, int n0, int rows_n, int wn, int lane) {
+  const bool has = p.bias != nullptr;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(has ? p.bias + n0 : nullptr, has ? (uint32_t)rows_n * 2u : 0u);
+  const int base = (wn * 128 + 4 * (lane >> 5)) * 2;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    B.v[k] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rb, base + (32 * (k >> 2) + 8 * (k & 3)) * 2, 0, 0));
+}
+
+__device__ __forceinline__ float bias_at(const BiasQuads& B, int k, int r) {
+  const uint32_t w = (uint32_t)B.v[k][r >> 1];
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
 // Workgroup -> (token tile, weight tile). Workgroups are dealt round-robin to
 // the 8 XCDs, so first give each XCD a contiguous range of logical tiles, then
 // walk that range in groups of GM token tiles x all weight tiles (token tile
@@ -452,21 +475,18 @@ __device__ __forceinline__ void mma8(f32x16 (&acc)[4][2], const Frags& F) {
 // per lane) with non-temporal stores: whole 128-byte lines, no partial-line
 // writebacks.
 template <int EPI, int MF = 2>
-__device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Params& p, uint8_t* ep, int m0, int n0,
-                                            int rows_m, int rows_n, int wn, int wm, int lane) {
+__device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const BiasQuads& B, const Params& p,
+                                            uint8_t* ep, int m0, int n0, int rows_m, int rows_n, int wn, int wm,
+                                            int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nb = 8 * i + 2 * q + hi;
-      const int nl = wn * 128 + 4 * nb;
-      float b[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.bias != nullptr && nl < rows_n) {
-        const uint16_t* bp = p.bias + n0 + nl;
+      float b[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, bp[r]);
-      }
+      for (int r = 0; r < 4; ++r) b[r] = bias_at(B, 4 * i + q, r);
 #pragma unroll
       for (int j = 0; j < MF; ++j) {
         const int m = 32 * j + r32;
@@ -555,9 +575,11 @@ __global__ __launch_bounds__(NT8, 1) void linear_prequant_pp(Params p) {
     mma8(acc, F1);
   }
   __builtin_amdgcn_sched_barrier(0);
+  BiasQuads B;
+  load_bias_quads(B, p, n0, rows_n, wn, lane);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  store_tile8<EPI>(acc, p, smem + wave * 16384, m0, n0, rows_m, rows_n, wn, wm, lane);
+  store_tile8<EPI>(acc, B, p, smem + wave * 16384, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
 
 template <int EPI>
@@ -815,21 +837,17 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
 // M are written as zero codes and scales (the slab's pad rows); columns past
 // N are dropped.
 template <int EPI>
-__device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Params& p, uint8_t* ep, int m0, int n0,
-                                             int rows_n, int wn, int wm, int lane) {
+__device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const BiasQuads& B, const Params& p,
+                                             uint8_t* ep, int m0, int n0, int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nb = 8 * i + 2 * q + hi;
-      const int nl = wn * 128 + 4 * nb;
-      float b[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.bias != nullptr && nl < rows_n) {
-        const uint16_t* bp = p.bias + n0 + nl;
+      float b[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, bp[r]);
-      }
+      for (int r = 0; r < 4; ++r) b[r] = bias_at(B, 4 * i + q, r);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = 32 * j + r32;
@@ -959,14 +977,16 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   }
   if (j < nh) half_step(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
   __builtin_amdgcn_sched_barrier(0);
+  BiasQuads B;
+  if constexpr (OUT != OUT_PART) load_bias_quads(B, p, n0, rows_n, wn, lane);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   if constexpr (OUT == OUT_Q)
-    store_tile_q<EPI>(acc, p, smem + wave * 32768, m0, n0, rows_n, wn, wm, lane);
+    store_tile_q<EPI>(acc, B, p, smem + wave * 32768, m0, n0, wn, wm, lane);
   else if constexpr (OUT == OUT_PART)
     store_tile_part(acc, p, tm * p.tiles_n + tn, ks, m0, wave, wm, lane);
   else
-    pp::store_tile8<EPI, 4>(acc, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
+    pp::store_tile8<EPI, 4>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
 
 // Split-K reduction: one thread per 16-byte chunk of the partial tiles (the
