@@ -5,8 +5,9 @@ leg of the bench are the only callers. The product path (the HIP library and
 its Python binding) never imports, calls or links anything here, and nothing
 here imports the product package.
 
-Everything is plain numpy in float64. See ``oracle/mx_oracle.py`` for the
-definitions and the passages each function follows.
+Everything is plain numpy in float64 (float32 where the pages fix FP32
+scales). ``oracle/mx_oracle.py`` is the MXFP8 scheme, ``oracle/pc_oracle.py``
+the per-output-channel FP8 scheme; each function cites the passage it follows.
 """
 
 from .mx_oracle import (  # noqa: F401
@@ -27,3 +28,4 @@ from .mx_oracle import (  # noqa: F401
     quantize_mx,
     tolerance,
 )
+from .pc_oracle import QMAX, dequantize_pc, linear_pc_ref, quantize_pc  # noqa: F401
