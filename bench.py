@@ -263,6 +263,33 @@ def denoise_step(torch, synth, dev, steps=2, warmup=1):
     return res
 
 
+def per_channel_step(torch, mx, synth, dev, M, K, N, steps=10, warmup=3):
+    """The per-output-channel FP8 scheme on the headline shape: per-token
+    activation quantization (f32 row scales) + the GEMM with the row scales
+    in its epilogue; weights quantized per output channel before timing."""
+    x = synth.make_activation_device(M, K, 300, dev)
+    w = mx.mx_pc_quantize_weight_slab(synth.make_weight_device(N, K, 300, dev))
+    b = synth.make_bias(N, 300).to(dev)
+    xs = mx.mx_pc_quantize_act_slab(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    total, (q_ms, g_ms) = timed_step(
+        torch, [lambda: mx.mx_pc_quantize_act_slab(x, xs), lambda: mx.mx_pc_linear_slab(xs, w, b, y=y)], steps, warmup)
+    ms = total / steps
+    flop = 2.0 * M * N * K
+    act_bytes = M * K * (2 + 1) + M * 4
+    res = {
+        "step_ms": round(ms, 4),
+        "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
+        "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
+        "gemm_ms": round(mean(g_ms), 4),
+        "quantize_act_ms": round(mean(q_ms), 4),
+        "quantize_act_GBps": round(act_bytes / (mean(q_ms) * 1e-3) / 1e9, 1),
+    }
+    del x, w, xs, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -407,6 +434,7 @@ def main():
         del y
         out["extra"]["other_workloads"] = other_workloads(torch, mx, synth, dev)
         out["extra"]["denoise_step"] = denoise_step(torch, synth, dev)
+        out["extra"]["per_channel_fp8"] = per_channel_step(torch, mx, synth, dev, M, K, N)
 
     if not args.no_cpu_baseline:
         del x, xsl, rowmajor

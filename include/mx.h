@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 5
+#define MX_ABI_VERSION 6
 
 typedef enum {
   MX_OK = 0,
@@ -217,6 +217,48 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
                           const uint8_t* wq, const uint8_t* ws, int64_t N,
                           const void* bias, int epilogue, void* y, int splits,
                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-output-channel FP8: the second FP8 scheme of the pages ("Wan2.2 I2V
+ * A14B, four-step 720p: native LightX2V FP8 and NVFP4", section "Conversion
+ * and compatibility": E4M3 weights with per-output-channel FP32 scales,
+ * nearest rounding; "Model Quantization Techniques", mode table: channel-
+ * symmetric FP8 weights, channel-dynamic-symmetric FP8 activations with the
+ * row scale max(abs(x)) / qmax, qmax 448 with FP32 accumulation). One f32
+ * scale per row instead of one E8M0 scale per 32 elements:
+ *   s    = f32(max_k |x[r][k]|) / 448        (f32 division, nearest even)
+ *   code = E4M3(f32(x[r][k]) / s)            (f32 division, then nearest even,
+ *                                             saturating at +-448, sign of
+ *                                             zero kept)
+ *   s == 0: every code a signed zero. A row holding NaN or Inf: s = NaN and
+ *   every code 0x7F.
+ * Codes use the slab layout above ([K/64][R][64], R = mx_slab_rows(rows),
+ * pad rows zero); scales are f32 [R] (pad rows 0).
+ * ------------------------------------------------------------------------ */
+
+/* Dynamic per-token quantization of bf16 x [M][ldx] (ldx >= K, ldx % 8 == 0,
+ * K % 64 == 0): q uint8 [K/64][RM][64], s f32 [RM]. Codes 16-byte aligned,
+ * scales 4-byte aligned; outputs must not overlap x or each other. */
+int mx_pc_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx,
+                            uint8_t* q, float* s, void* stream);
+
+/* Per-output-channel quantization of weights w [N][ldw] of type wdtype
+ * (MX_DT_F32 or MX_DT_BF16; ldw * sizeof(element) % 16 == 0): q uint8
+ * [K/64][RN][64], s f32 [RN]. */
+int mx_pc_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
+                               uint8_t* q, float* s, void* stream);
+
+/* The per-channel FP8 linear:
+ *   y[m][n] = bf16_rne( epi( xs[m] * ws[n] * sum_k dec(xq[m][k]) dec(wq[n][k])
+ *                            + f32(bias[n]) ) )
+ * with products exact and sums in f32 (the block-scaled MFMAs of the MX path
+ * with unit scales; the row scales are applied to the f32 sums). Operands in
+ * the layout above; bias f16 [N] or NULL; y bf16 [M][N]. K % 64 == 0, N % 16
+ * == 0 (else MX_ERR_UNSUPPORTED); codes and y 16-byte aligned, scales 4-byte
+ * aligned; y must not overlap an input. */
+int mx_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K,
+                      const uint8_t* wq, const float* ws, int64_t N,
+                      const void* bias, int epilogue, void* y, void* stream);
 
 #ifdef __cplusplus
 }

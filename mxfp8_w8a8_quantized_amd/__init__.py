@@ -48,6 +48,9 @@ SIGNATURES = {
     "mx_linear_splitk_ws_bytes": ([_I64, _I64, _INT], _I64),
     "mx_linear_splitk_choose": ([_I64, _I64, _I64], _INT),
     "mx_linear_slab_splitk": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
+    "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
+    "mx_pc_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
+    "mx_pc_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
 }
 
 
@@ -405,6 +408,99 @@ def mx_linear_slab_splitk(x, w, bias=None, gelu=False, y=None, splits=None, work
             lib().mx_linear_slab_splitk(
                 _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), splits,
                 _ptr(workspace), workspace.numel(), _stream(dev),
+            )
+        )
+    return y
+
+
+class PCSlab(NamedTuple):
+    """A per-channel FP8 operand: codes q uint8 [K/64, R, 64] (slab layout)
+    and one f32 scale per row s [R], R = mx_slab_rows(rows); pad rows zero."""
+
+    q: torch.Tensor
+    s: torch.Tensor
+    rows: int
+
+    @property
+    def K(self):
+        return self.q.shape[0] * 64
+
+
+def _pc_out(rows, K, dev, out):
+    R = mx_slab_rows(rows)
+    if out is None:
+        return PCSlab(
+            torch.empty((K // 64, R, 64), dtype=torch.uint8, device=dev),
+            torch.empty((R,), dtype=torch.float32, device=dev),
+            rows,
+        )
+    _need(out.q, "out.q", torch.uint8, dev)
+    _need(out.s, "out.s", torch.float32, dev)
+    if out.q.shape != (K // 64, R, 64) or out.s.shape != (R,) or out.rows != rows:
+        raise ValueError(f"out must hold [{K // 64}, {R}, 64] codes and [{R}] scales for {rows} rows")
+    return out
+
+
+def mx_pc_quantize_act_slab(x, out=None):
+    """bf16 [M, K] (rows may be strided, K % 64 == 0) -> PCSlab: per-token
+    FP8 codes and f32 row scales (max |x| / 448)."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    if K % 64 != 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    dev = x.device
+    out = _pc_out(M, K, dev, out)
+    ld = x.stride(0) if M > 1 else K
+    with torch.cuda.device(dev):
+        _check(lib().mx_pc_quantize_act_slab(_ptr(x), M, K, ld, _ptr(out.q), _ptr(out.s), _stream(dev)))
+    return out
+
+
+def mx_pc_quantize_weight_slab(w, out=None):
+    """fp32 or bf16 [N, K] -> PCSlab: per-output-channel FP8 codes and f32 scales."""
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be 2-D with unit column stride")
+    dt = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}.get(w.dtype)
+    if dt is None:
+        raise TypeError(f"w must be float32 or bfloat16, got {w.dtype}")
+    N, K = w.shape
+    if K % 64 != 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    dev = w.device
+    out = _pc_out(N, K, dev, out)
+    ld = w.stride(0) if N > 1 else K
+    with torch.cuda.device(dev):
+        _check(lib().mx_pc_quantize_weight_slab(_ptr(w), dt, N, K, ld, _ptr(out.q), _ptr(out.s), _stream(dev)))
+    return out
+
+
+def mx_pc_linear_slab(x, w, bias=None, gelu=False, y=None):
+    """y = bf16(epi(xs[m] ws[n] (dec(xq) @ dec(wq)^T) + bias)) on PCSlab operands."""
+    dev = x.q.device
+    for name, t, dt in (("x.q", x.q, torch.uint8), ("x.s", x.s, torch.float32), ("w.q", w.q, torch.uint8),
+                        ("w.s", w.s, torch.float32)):
+        _need(t, name, dt, dev)
+    M, N, K = x.rows, w.rows, x.K
+    if w.K != K:
+        raise ValueError(f"x has K = {K}, w has K = {w.K}")
+    for name, sl in (("x", x), ("w", w)):
+        R = mx_slab_rows(sl.rows)
+        if sl.q.shape != (K // 64, R, 64) or sl.s.shape != (R,):
+            raise ValueError(f"{name} is not a per-channel slab of {sl.rows} rows and K = {K}")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be f16 [N]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_pc_linear_slab(
+                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _stream(dev)
             )
         )
     return y

@@ -163,6 +163,29 @@ int check_slab_output(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K
   return MX_OK;
 }
 
+// Per-channel quantizer arguments: x [rows][ld] of dtype dt; slab codes, f32 row scales.
+int check_pc_quantize(const void* x, int dt, int64_t rows, int64_t K, int64_t ld, const uint8_t* q,
+                      const float* sc) {
+  int st;
+  if (dt != MX_DT_BF16 && dt != MX_DT_F32) return fail(MX_ERR_INVALID_ARGUMENT, "unknown weight dtype %d", dt);
+  if ((st = check_rows("rows", rows)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (K % 64 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
+  const int64_t es = dt == MX_DT_F32 ? 4 : 2;
+  if (ld < K || (ld * es) % 16 != 0)
+    return fail(MX_ERR_INVALID_ARGUMENT, "pitch %lld must be >= K with 16-byte aligned rows", (long long)ld);
+  if (rows == 0) return MX_OK;
+  if (x == nullptr || q == nullptr || sc == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sc, 4))
+    return fail(MX_ERR_INVALID_ARGUMENT, "input and codes must be 16-byte aligned, scales 4-byte aligned");
+  const uint64_t R = (uint64_t)mx::slab_rows(rows);
+  const uint64_t xbytes = ((uint64_t)(rows - 1) * ld + K) * es;
+  const uint64_t nq = R * K, ns = R * 4;
+  if (overlap(q, nq, x, xbytes) || overlap(sc, ns, x, xbytes) || overlap(q, nq, sc, ns))
+    return fail(MX_ERR_INVALID_ARGUMENT, "outputs overlap an input or each other");
+  return check_device();
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,6 +405,50 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
   (void)hipGetLastError();
   return finish(mx::launch_linear_slab_splitk(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, (float*)workspace,
                                               (hipStream_t)stream),
+                "linear launch");
+}
+
+int mx_pc_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, float* s, void* stream) {
+  const int st = check_pc_quantize(x, MX_DT_BF16, M, K, ldx, q, s);
+  if (st != MX_OK || M == 0) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_pc_quantize_slab(0, x, M, K, ldx, q, s, (hipStream_t)stream), "quantize launch");
+}
+
+int mx_pc_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q, float* s,
+                               void* stream) {
+  const int st = check_pc_quantize(w, wdtype, N, K, ldw, q, s);
+  if (st != MX_OK || N == 0) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_pc_quantize_slab(wdtype == MX_DT_F32 ? 1 : 0, w, N, K, ldw, q, s, (hipStream_t)stream),
+                "quantize launch");
+}
+
+int mx_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq, const float* ws,
+                      int64_t N, const void* bias, int epilogue, void* y, void* stream) {
+  int st;
+  if ((st = check_rows("M", M)) != MX_OK) return st;
+  if ((st = check_k(K)) != MX_OK) return st;
+  if (K % 64 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a multiple of 64 for the slab layout", (long long)K);
+  if (N < 0) return fail(MX_ERR_INVALID_ARGUMENT, "N = %lld is negative", (long long)N);
+  if (N > kMaxKN) return fail(MX_ERR_UNSUPPORTED, "N = %lld exceeds the supported 2^20", (long long)N);
+  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH)
+    return fail(MX_ERR_INVALID_ARGUMENT, "unknown epilogue %d", epilogue);
+  if (M == 0 || N == 0) return MX_OK;
+  if (N % 16 != 0) return fail(MX_ERR_UNSUPPORTED, "N = %lld must be a multiple of 16", (long long)N);
+  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr || y == nullptr)
+    return fail(MX_ERR_INVALID_ARGUMENT, "NULL operand or output pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xs, 4) || !aligned(ws, 4) || !aligned(y, 16))
+    return fail(MX_ERR_INVALID_ARGUMENT, "codes and y must be 16-byte aligned, scales 4-byte aligned");
+  if (bias != nullptr && !aligned(bias, 2)) return fail(MX_ERR_INVALID_ARGUMENT, "bias must be 2-byte aligned");
+  const uint64_t RM = (uint64_t)mx::slab_rows(M), RN = (uint64_t)mx::slab_rows(N);
+  const uint64_t yb = (uint64_t)M * N * 2;
+  if (overlap(y, yb, xq, RM * K) || overlap(y, yb, xs, RM * 4) || overlap(y, yb, wq, RN * K) ||
+      overlap(y, yb, ws, RN * 4) || overlap(y, yb, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_pc_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
                 "linear launch");
 }
 

@@ -65,6 +65,8 @@ struct Params {
   uint8_t* hq;           // requantized output: codes slab [N/64][RM][64] (or null)
   uint8_t* hs;           //                     scales slab [N/64][RM][2]
   float* part;           // split-K partial sums (or null), see slab::store_tile_part
+  const float* sx;       // per-channel FP8: f32 scale per token row [RM] (or null)
+  const float* sw;       //                  f32 scale per weight row [RN]
   int splits;            // K ranges per tile (split-K), else 1
   int M, N, K;
   int tiles_m, tiles_n;
@@ -474,10 +476,13 @@ __device__ __forceinline__ void mma8(f32x16 (&acc)[4][2], const Frags& F) {
 // distinct bank pairs), then 4 rows x 256 B per store instruction (16 bytes
 // per lane) with non-temporal stores: whole 128-byte lines, no partial-line
 // writebacks.
-template <int EPI, int MF = 2>
+// PC (per-channel FP8): each accumulator is first multiplied by its token
+// row's and weight row's f32 scales, read from the LDS table `tab`
+// ([0, 256) weight rows of the tile, [256, 512) token rows).
+template <int EPI, int MF = 2, bool PC = false>
 __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const BiasQuads& B, const Params& p,
                                             uint8_t* ep, int m0, int n0, int rows_m, int rows_n, int wn, int wm,
-                                            int lane) {
+                                            int lane, const float* tab = nullptr) {
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -487,12 +492,20 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Bi
       float b[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) b[r] = bias_at(B, 4 * i + q, r);
+      f32x4 swq = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (PC) swq = *(const f32x4*)(tab + wn * 128 + 4 * nb);
 #pragma unroll
       for (int j = 0; j < MF; ++j) {
         const int m = 32 * j + r32;
         float v[4];
+        if constexpr (PC) {
+          const float sxm = tab[256 + wm * 32 * MF + m];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] + b[r]);
+          for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] * (sxm * swq[r]) + b[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] + b[r]);
+        }
         const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
         const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
         *(i32x2*)(ep + m * 256 + ((nb ^ (m & 31)) << 3)) =
@@ -645,17 +658,20 @@ struct Src {
 // 4 wave + 3 of both code operands (1 KB each; lane L takes row L/4, global
 // chunk (L%4) ^ (L/16) into LDS slot L%4) and one 256-byte half of the
 // weight (waves 0, 1) or token (waves 2, 3) scales.
+template <bool PC>
 __device__ __forceinline__ void issue_half(const Src& S, uint8_t* smem, int j, int wave, int lane) {
   uint8_t* reg = smem + (j & 3) * REGION;
   const bool valid = j < S.nh;
   const uint32_t nc = valid ? 16384u : 0u, ns = valid ? 512u : 0u;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(S.w + (uint64_t)j * S.w_slab, nc);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x + (uint64_t)j * S.x_slab, nc);
-  const bool wscale = wave < 2;
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(wscale ? S.ws + (uint64_t)j * (S.w_slab >> 5) : S.xs + (uint64_t)j * (S.x_slab >> 5), ns);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(reg + (wscale ? R_WS : R_XS) + (wave & 1) * 256), 4,
-                                           lane * 4, (wave & 1) * 256, 0, 0);
+  if constexpr (!PC) {
+    const bool wscale = wave < 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(wscale ? S.ws + (uint64_t)j * (S.w_slab >> 5) : S.xs + (uint64_t)j * (S.x_slab >> 5), ns);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(reg + (wscale ? R_WS : R_XS) + (wave & 1) * 256), 4,
+                                             lane * 4, (wave & 1) * 256, 0, 0);
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = wave * 4 + u;
@@ -674,6 +690,7 @@ struct Frags {
 // Fragments of a region for the 32x32x64 MFMA: lane l, fragment f reads row
 // base + 32 f + l%32, K bytes [16 (l/32), +16) and [32 + 16 (l/32), +16) of
 // the 64, and the scale of group l/32 of the half-step.
+template <bool PC>
 __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
   const int sw = (r32 >> 2) & 3;
@@ -684,7 +701,7 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
     const uint8_t* ra = reg + R_W + row * 64;
     const i32x4 a0 = *(const i32x4*)(ra + c0), a1 = *(const i32x4*)(ra + c1);
     F.a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    F.sa[f] = reg[R_WS + row * 2 + hi];
+    F.sa[f] = PC ? 127 : reg[R_WS + row * 2 + hi];
   }
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
@@ -692,16 +709,23 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
     const uint8_t* rb = reg + R_X + row * 64;
     const i32x4 b0 = *(const i32x4*)(rb + c0), b1 = *(const i32x4*)(rb + c1);
     F.b[f] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    F.sb[f] = reg[R_XS + row * 2 + hi];
+    F.sb[f] = PC ? 127 : reg[R_XS + row * 2 + hi];
   }
 }
 
+// Per-channel FP8 (PC) runs the same MFMAs with unit block scales (E8M0
+// 127 = 2^0); its row scales are applied in the epilogue.
+template <bool PC>
 __device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const Frags& F) {
   static_for<0, 4>([&](auto I) {
     constexpr int i = decltype(I)::value;
     static_for<0, 4>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, F.sa[i], 0, F.sb[j]);
+      if constexpr (PC)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+      else
+        acc[i][j] =
+            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, F.sa[i], 0, F.sb[j]);
     });
   });
 }
@@ -797,6 +821,21 @@ struct Slot {
   static constexpr int d = I < 9 ? (I == 0 ? 8 : I - 1) : -1;  // load piece, or none
 };
 
+// Per-channel FP8 has no block scales: read pieces 16..23 and load piece 8
+// (the scale DMA) drop out; the other pieces keep their slots.
+template <bool PC>
+constexpr int loads_per_half() { return PC ? LOADS_PER_HALF - 1 : LOADS_PER_HALF; }
+template <bool PC, int R>
+constexpr bool has_read() { return !PC || R < 16; }
+template <bool PC, int I>
+constexpr int slot_reads() {
+  int n = 0;
+  for (int r = Slot<I>::r0; r < Slot<I>::r1; ++r) n += (!PC || r < 16) ? 1 : 0;
+  return n;
+}
+template <bool PC, int I>
+constexpr bool slot_dma() { return Slot<I>::d >= 0 && !(PC && Slot<I>::d == 8); }
+
 // Half-step j. The lgkmcnt(0) in the wait keeps any wave's refill from
 // overtaking another wave's last reads of the region being refilled. The LDS
 // reads of the next fragments (region (j+1) % 4) and the refill DMAs of
@@ -805,10 +844,11 @@ struct Slot {
 // the scheduling groups put each slot's reads and DMA behind one MFMA: with
 // one wave per SIMD, this is what keeps the MFMA pipe fed and the address
 // path free of bursts.
+template <bool PC>
 __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
                                           int j, int wave, int wn, int wm, int lane) {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS_PER_HALF) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * loads_per_half<PC>()) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   const FragAddr A = frag_addr(smem + ((j + 1) & 3) * REGION, wn, wm, lane);
@@ -816,16 +856,18 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
   static_for<0, 16>([&](auto I) {
     constexpr int i = decltype(I)::value;
     using SL = Slot<i>;
-    static_for<SL::r0, SL::r1>([&](auto Rr) { read_piece<decltype(Rr)::value>(nxt, A); });
-    if constexpr (SL::d >= 0) load_piece<SL::d>(L, S, wave, lane);
+    static_for<SL::r0, SL::r1>([&](auto Rr) {
+      constexpr int r = decltype(Rr)::value;
+      if constexpr (has_read<PC, r>()) read_piece<r>(nxt, A);
+    });
+    if constexpr (slot_dma<PC, i>()) load_piece<SL::d>(L, S, wave, lane);
   });
-  mma16(acc, cur);
+  mma16<PC>(acc, cur);
   static_for<0, 16>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    using SL = Slot<i>;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if constexpr (SL::r1 > SL::r0) __builtin_amdgcn_sched_group_barrier(0x100, SL::r1 - SL::r0, 0);  // its reads
-    if constexpr (SL::d >= 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // its DMA
+    if constexpr (slot_reads<PC, i>() > 0) __builtin_amdgcn_sched_group_barrier(0x100, slot_reads<PC, i>(), 0);
+    if constexpr (slot_dma<PC, i>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // its DMA
   });
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -922,11 +964,18 @@ __device__ __forceinline__ void store_tile_part(const f32x16 (&acc)[4][4], const
   }
 }
 
-enum { OUT_Y = 0, OUT_Q = 1, OUT_PART = 2 };
+// Outputs: bf16 y; the requantized MX slab of y; split-K partial sums; bf16 y
+// of the per-channel FP8 linear (unit block scales, row scales in the
+// epilogue from a 2 KB LDS table past the ring: [0, 256) weight rows n0..,
+// [256, 512) token rows m0..).
+enum { OUT_Y = 0, OUT_Q = 1, OUT_PART = 2, OUT_PCY = 3 };
+constexpr int PC_TABLE = LDS;  // byte offset of the per-channel scale table
+constexpr int LDS_PC = LDS + 2048;
 
 template <int EPI, int OUT>
 __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr bool PC = OUT == OUT_PCY;
   int tm, tn;
   int bid = blockIdx.x, ks = 0;
   if constexpr (OUT == OUT_PART) {
@@ -953,8 +1002,8 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   S.x_slab = (uint64_t)p.tiles_m * BM * 64;
   S.w = p.wq + (size_t)n0 * 64 + h0 * S.w_slab;
   S.x = p.x + (size_t)m0 * 64 + h0 * S.x_slab;
-  S.ws = p.ws + (size_t)n0 * 2 + h0 * (S.w_slab >> 5);
-  S.xs = p.xs + (size_t)m0 * 2 + h0 * (S.x_slab >> 5);
+  S.ws = PC ? nullptr : p.ws + (size_t)n0 * 2 + h0 * (S.w_slab >> 5);
+  S.xs = PC ? nullptr : p.xs + (size_t)m0 * 2 + h0 * (S.x_slab >> 5);
   S.nh = nh_wg;
   S.voff = (lane >> 2) * 64 + (((lane & 3) ^ (lane >> 4)) << 4);
 
@@ -964,34 +1013,49 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  issue_half(S, smem, 0, wave, lane);
-  issue_half(S, smem, 1, wave, lane);
-  issue_half(S, smem, 2, wave, lane);
-  issue_half(S, smem, 3, wave, lane);
+  issue_half<PC>(S, smem, 0, wave, lane);
+  issue_half<PC>(S, smem, 1, wave, lane);
+  issue_half<PC>(S, smem, 2, wave, lane);
+  issue_half<PC>(S, smem, 3, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * LOADS_PER_HALF) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * loads_per_half<PC>()) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   Frags F0, F1;
-  read_frags(F0, smem, wn, wm, lane);
+  read_frags<PC>(F0, smem, wn, wm, lane);
   const int nh = S.nh;
   int j = 0;
   for (; j + 1 < nh; j += 2) {
-    half_step(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
-    half_step(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
+    half_step<PC>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+    half_step<PC>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
   }
-  if (j < nh) half_step(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+  if (j < nh) half_step<PC>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
   __builtin_amdgcn_sched_barrier(0);
   BiasQuads B;
   if constexpr (OUT != OUT_PART) load_bias_quads(B, p, n0, rows_n, wn, lane);
+  float scw = 0.f, scx = 0.f;
+  if constexpr (PC) {
+    // One weight-row and one token-row scale per thread; zero past N and M.
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.sw + n0, (uint32_t)rows_n * 4u);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.sx + m0, (uint32_t)rows_m * 4u);
+    scw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, threadIdx.x * 4, 0, 0));
+    scx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, threadIdx.x * 4, 0, 0));
+  }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  if constexpr (PC) {
+    float* tab = (float*)(smem + PC_TABLE);
+    tab[threadIdx.x] = scw;
+    tab[256 + threadIdx.x] = scx;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   __builtin_amdgcn_s_barrier();
   if constexpr (OUT == OUT_Q)
     store_tile_q<EPI>(acc, B, p, smem + wave * 32768, m0, n0, wn, wm, lane);
   else if constexpr (OUT == OUT_PART)
     store_tile_part(acc, p, tm * p.tiles_n + tn, ks, m0, wave, wm, lane);
   else
-    pp::store_tile8<EPI, 4>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane);
+    pp::store_tile8<EPI, 4, PC>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane,
+                                (const float*)(smem + PC_TABLE));
 }
 
 // Split-K reduction: one thread per 16-byte chunk of the partial tiles (the
@@ -1036,12 +1100,13 @@ template <int EPI, int OUT = OUT_Y>
 hipError_t launch(const Params& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
   auto kern = linear_slab_kernel<EPI, OUT>;
+  constexpr int lds = OUT == OUT_PCY ? LDS_PC : LDS;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT4), LDS, st, p);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT4), lds, st, p);
   return hipGetLastError();
 }
 
@@ -1082,6 +1147,8 @@ hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
   p.hq = nullptr;
   p.hs = nullptr;
   p.part = nullptr;
+  p.sx = nullptr;
+  p.sw = nullptr;
   p.splits = 1;
   p.M = (int)M;
   p.N = (int)N;
@@ -1108,6 +1175,8 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
   p.hq = nullptr;
   p.hs = nullptr;
   p.part = nullptr;
+  p.sx = nullptr;
+  p.sw = nullptr;
   p.splits = 1;
   p.M = (int)M;
   p.N = (int)N;
@@ -1131,6 +1200,8 @@ hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int6
   p.hq = hq;
   p.hs = hs;
   p.part = nullptr;
+  p.sx = nullptr;
+  p.sw = nullptr;
   p.splits = 1;
   p.M = (int)M;
   p.N = (int)N;
@@ -1154,6 +1225,8 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
   p.hq = nullptr;
   p.hs = nullptr;
   p.part = part;
+  p.sx = nullptr;
+  p.sw = nullptr;
   p.splits = splits;
   p.M = (int)M;
   p.N = (int)N;
@@ -1169,6 +1242,30 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
   else
     hipLaunchKernelGGL(slab::splitk_reduce_kernel<0>, dim3(nred), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                 const float* ws, int64_t N, const void* bias, int epi, void* y, hipStream_t stream) {
+  Params p;
+  p.x = xq;
+  p.xs = nullptr;
+  p.wq = wq;
+  p.ws = nullptr;
+  p.bias = (const uint16_t*)bias;
+  p.y = (uint16_t*)y;
+  p.hq = nullptr;
+  p.hs = nullptr;
+  p.part = nullptr;
+  p.sx = xs;
+  p.sw = ws;
+  p.splits = 1;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const int nwg = p.tiles_m * p.tiles_n;
+  return epi == 1 ? slab::launch<1, slab::OUT_PCY>(p, nwg, stream) : slab::launch<0, slab::OUT_PCY>(p, nwg, stream);
 }
 
 }  // namespace mx

@@ -53,4 +53,16 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
                                      const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
                                      float* part, hipStream_t stream);
 
+// Per-output-channel FP8: rows of x (bf16, kind 0, or f32, kind 1; pitch ld)
+// to E4M3 codes in the slab layout q [K/64][R][64] and one f32 scale per row
+// s [R] (R = slab_rows(rows); pad rows zero). K % 64 == 0.
+hipError_t launch_pc_quantize_slab(int kind, const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, float* s,
+                                   hipStream_t stream);
+
+// The slab GEMM on per-channel operands: codes as for launch_linear_slab,
+// scales f32 per token row (xs [RM]) and per weight row (ws [RN]);
+// y = bf16(epi(xs[m] ws[n] acc + bias[n])).
+hipError_t launch_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                 const float* ws, int64_t N, const void* bias, int epi, void* y, hipStream_t stream);
+
 }  // namespace mx

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 5
+    assert L.mx_abi_version() == 6
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -206,6 +206,29 @@ def test_splitk_rejects_bad_arguments(L):
     assert call(wsp=A) == 1  # workspace overlaps the token codes
     assert call(y=E) == 1  # y overlaps the workspace
     assert call(epi=7) == 1
+    assert call(N=264) == 2
+    assert call(M=0) == 0 and call(N=0) == 0
+
+
+def test_pc_calls_reject_bad_arguments(L):
+    qa = L.mx_pc_quantize_act_slab
+    qw = L.mx_pc_quantize_weight_slab
+    E = 0x50000000
+    assert qa(P(A), 8, 96, 96, P(B), P(E), P(0)) == 1  # K % 64
+    assert qa(P(A), 8, 64, 60, P(B), P(E), P(0)) == 1  # pitch < K
+    assert qa(P(A), 8, 64, 64, P(0), P(E), P(0)) == 1
+    assert qa(P(A), 8, 64, 64, P(B), P(E + 2), P(0)) == 1  # scales not 4-byte aligned
+    assert qa(P(A), 8, 64, 64, P(A), P(E), P(0)) == 1  # codes overlap x
+    assert qa(P(A), 0, 64, 64, P(B), P(E), P(0)) == 0
+    assert qw(P(A), 7, 8, 64, 64, P(B), P(E), P(0)) == 1  # dtype
+    assert qw(P(A), 1, 8, 64, 66, P(B), P(E), P(0)) == 1  # f32 pitch not 16-byte aligned
+    f = L.mx_pc_linear_slab
+
+    def call(xq=A, xs=E, M=8, K=128, wq=C, ws=E + 4096, N=256, epi=0, y=D):
+        return f(P(xq), P(xs), M, K, P(wq), P(ws), N, P(0), epi, P(y), P(0))
+
+    assert call(K=96) == 1 and call(epi=5) == 1 and call(xs=0) == 1 and call(y=0) == 1
+    assert call(ws=E + 2) == 1 and call(y=C) == 1
     assert call(N=264) == 2
     assert call(M=0) == 0 and call(N=0) == 0
 
