@@ -148,3 +148,33 @@ def test_pc_linear_qkv_full_size():
     wq, wsr = oracle.quantize_pc(w.numpy())
     yref, S = oracle.linear_pc_ref(xq, xsr, wq, wsr, bias=f64(b))
     assert_linear_close(y[rows], yref, S, what="pc qkv")
+
+
+def test_pc_quantizer_quotients_at_rounding_ties():
+    # Rows whose quotients x / s land on, and one or two float32 ulps around,
+    # E4M3 rounding midpoints (ties go to the even code), under scales with
+    # long significands: the quantizer's quotient must be the correctly
+    # rounded one for the codes to match the oracle's.
+    rng = np.random.default_rng(5)
+    mags = oracle.e4m3_decode(np.arange(0, 127)).astype(np.float64)
+    mids = (mags[:-1] + mags[1:]) / 2  # E4M3 rounding boundaries, exact in float32
+    rows = []
+    for _ in range(64):
+        amax = np.float32(rng.uniform(0.5, 64.0))
+        s = np.float32(amax / np.float32(448.0))
+        targets = rng.choice(mids, 255)
+        vals = (targets * np.float64(s)).astype(np.float32)  # quotient within an ulp or two of a midpoint
+        for d in (-2, -1, 1, 2):
+            idx = rng.integers(0, 255, 32)
+            for _ in range(abs(d)):
+                vals[idx] = np.nextafter(vals[idx], np.float32(np.sign(d) * np.inf))
+        vals = np.concatenate([[amax], np.minimum(np.abs(vals), amax) * rng.choice([-1, 1], 255)]).astype(np.float32)
+        rows.append(vals)
+    w = torch.from_numpy(np.stack(rows))  # [64, 256] f32: the weight path takes f32
+    sl = mx().mx_pc_quantize_weight_slab(w.to(dev()))
+    torch.cuda.synchronize()
+    check_quant(sl, w.numpy())
+    xb = w.to(torch.bfloat16)  # and the activation path, on the bf16-rounded rows
+    sl = mx().mx_pc_quantize_act_slab(xb.to(dev()))
+    torch.cuda.synchronize()
+    check_quant(sl, xb.float().numpy())
