@@ -255,9 +255,12 @@ template <int EPI>
 __device__ __forceinline__ float epilogue(float v) {
   if (EPI == 1) {
     // GELU, tanh form, as v * sigmoid(2u) = 0.5 v (1 + tanh(u)),
-    // u = sqrt(2/pi) (v + 0.044715 v^3); this form has no cancellation.
+    // u = sqrt(2/pi) (v + 0.044715 v^3); this form has no cancellation. The
+    // hardware exp2 and reciprocal (about 1 ulp each) replace the IEEE
+    // division, whose ~10 instructions per output made the GELU linear 6%
+    // slower; the result is rounded to bf16 (2^-8) right after.
     const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-    return v / (1.0f + __expf(-2.0f * u));
+    return v * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
   }
   return v;
 }
