@@ -28,7 +28,9 @@ Prints ONE JSON line. Besides the contract fields it carries
                 linears (40 blocks) back to back.
 
 Modes for profiling: --profile step|rowmajor|fused runs only those kernels
-(steps times, no oracle); --profile-copy runs a 1 GiB device copy used to
+(steps times, no oracle); --profile workloads runs the other workloads (FFN
+pair, cross-attention set, 128-token linear, per-channel FP8 step, one whole
+denoise step) twice each; --profile-copy runs a 1 GiB device copy used to
 calibrate the HBM byte counters.
 """
 
@@ -66,7 +68,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--profile", choices=["step", "rowmajor", "fused"], help="run only these kernels")
+    ap.add_argument("--profile", choices=["step", "rowmajor", "fused", "workloads"], help="run only these kernels")
     ap.add_argument("--profile-copy", action="store_true", help="run only a 1 GiB device copy")
     return ap.parse_args()
 
@@ -324,6 +326,15 @@ def main():
         __graft_entry__.build()
 
     shape = synth.CONFIGS[WORKLOAD][0]
+    if args.profile == "workloads":
+        res = {
+            "other_workloads": other_workloads(torch, mx, synth, dev, steps=2, warmup=1),
+            "per_channel_fp8": per_channel_step(torch, mx, synth, dev, shape.M, shape.K, shape.N, steps=2, warmup=1),
+            "denoise_step": denoise_step(torch, synth, dev, steps=1, warmup=1),
+        }
+        print(json.dumps({"profiled": "workloads", "results": res}), flush=True)
+        return
+
     M, K, N = shape.M, shape.K, shape.N
     x_cpu = synth.make_activation(M, K, seed=0)
     w_cpu = synth.make_weight(N, K, seed=0)

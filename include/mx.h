@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 6
+#define MX_ABI_VERSION 7
 
 typedef enum {
   MX_OK = 0,
@@ -217,6 +217,29 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
                           const uint8_t* wq, const uint8_t* ws, int64_t N,
                           const void* bias, int epilogue, void* y, int splits,
                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes mx_linear_slab_balanced needs on the current device: the
+ * fp32 partial tiles of its split last round, 0 when it splits nothing; -1 on
+ * bad arguments (M, N < 0; K not a positive multiple of 64). */
+int64_t mx_linear_balanced_ws_bytes(int64_t M, int64_t K, int64_t N);
+
+/* mx_linear_slab with its last, partial round of tiles split over K. The
+ * T = ceil(M/256) * ceil(N/256) tiles run as full rounds of one tile per CU
+ * (C = the device's compute units) and a last round of T mod C tiles that
+ * would leave most CUs idle (75348 x 5120: 5900 tiles, 12 in the last round);
+ * those tiles are split into s = min(C / (T mod C), 8, K/128) K ranges, their
+ * fp32 partial sums reduced in fixed order (as mx_linear_slab_splitk). Tiles
+ * of the full rounds are bit-identical to mx_linear_slab's, the split ones
+ * equal up to the order of the fp32 sums; the split depends only on the shape
+ * and C, so results are deterministic on a given device. workspace: at least
+ * mx_linear_balanced_ws_bytes(M, K, N) bytes, 256-byte aligned, not
+ * overlapping an operand, bias or y (may be NULL when that is 0). Up to three
+ * kernels on `stream`; nothing is allocated. Other arguments and errors as
+ * mx_linear_slab. */
+int mx_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                            const uint8_t* wq, const uint8_t* ws, int64_t N,
+                            const void* bias, int epilogue, void* y,
+                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Per-output-channel FP8: the second FP8 scheme of the pages ("Wan2.2 I2V

@@ -48,6 +48,8 @@ SIGNATURES = {
     "mx_linear_splitk_ws_bytes": ([_I64, _I64, _INT], _I64),
     "mx_linear_splitk_choose": ([_I64, _I64, _I64], _INT),
     "mx_linear_slab_splitk": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
+    "mx_linear_balanced_ws_bytes": ([_I64, _I64, _I64], _I64),
+    "mx_linear_slab_balanced": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
@@ -408,6 +410,35 @@ def mx_linear_slab_splitk(x, w, bias=None, gelu=False, y=None, splits=None, work
             lib().mx_linear_slab_splitk(
                 _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), splits,
                 _ptr(workspace), workspace.numel(), _stream(dev),
+            )
+        )
+    return y
+
+
+def mx_linear_balanced_ws_bytes(M, K, N):
+    return lib().mx_linear_balanced_ws_bytes(M, K, N)
+
+
+def mx_linear_slab_balanced(x, w, bias=None, gelu=False, y=None, workspace=None):
+    """mx_linear_slab with the last, partial round of tiles split over K;
+    workspace: uint8 of at least mx_linear_balanced_ws_bytes(M, K, N) bytes
+    (allocated here when None and needed)."""
+    dev, M, N, K = _slab_linear_args(x, w, bias)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    need = mx_linear_balanced_ws_bytes(M, K, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_slab_balanced(
+                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _ptr(workspace),
+                0 if workspace is None else workspace.numel(), _stream(dev),
             )
         )
     return y

@@ -186,6 +186,15 @@ int check_pc_quantize(const void* x, int dt, int64_t rows, int64_t K, int64_t ld
   return check_device();
 }
 
+// Compute units of the current device (the balanced GEMM's round size).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -449,6 +458,44 @@ int mx_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K, 
   if ((st = check_device()) != MX_OK) return st;
   (void)hipGetLastError();
   return finish(mx::launch_pc_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
+                "linear launch");
+}
+
+int64_t mx_linear_balanced_ws_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN) return -1;
+  if (M == 0 || N == 0) return 0;
+  int64_t full;
+  int splits;
+  return mx::balanced_plan(M, K, N, cu_count(), &full, &splits);
+}
+
+int mx_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                            const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (y == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL y");
+  if (!aligned(y, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned");
+  const uint64_t ybytes = (uint64_t)M * N * 2;
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, y, ybytes, "y")) != MX_OK) return st;
+  const int ncu = cu_count();
+  int64_t full;
+  int splits;
+  const int64_t need = mx::balanced_plan(M, K, N, ncu, &full, &splits);
+  if (need > 0) {
+    if (workspace == nullptr || !aligned(workspace, 256))
+      return fail(MX_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)need);
+    if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, workspace, (uint64_t)need, "workspace")) != MX_OK)
+      return st;
+    if (overlap(workspace, (uint64_t)need, y, ybytes)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps y");
+  }
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear_slab_balanced(xq, xs, M, K, wq, ws, N, bias, epilogue, y, ncu, (float*)workspace,
+                                                (hipStream_t)stream),
                 "linear launch");
 }
 

@@ -39,6 +39,8 @@
 //
 // Ragged edges: buffer resources are rebased at the tile; rows past M (or N)
 // load as zero and their stores are dropped.
+#include <algorithm>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -53,7 +55,8 @@ constexpr int TILE_BYTES = 256 * BK;        // one operand, one stage
 constexpr int SCALE_BYTES = 4 * 256;        // one operand, one stage
 constexpr int LDS_BYTES = 4 * TILE_BYTES + 4 * SCALE_BYTES;
 constexpr int kDropOffset = 1 << 30;  // beyond every resource: the store is dropped
-constexpr int kStoreAux = 2;  // cache policy of the fast path's output stores: non-temporal
+constexpr int kStoreAux = 2;
+constexpr int64_t kMaxTailSplits = 8;  // as the split-K choice: partial traffic grows with it  // cache policy of the fast path's output stores: non-temporal
 
 struct Params {
   const uint8_t* x;   // bf16 tokens (fused) or E4M3 codes
@@ -68,6 +71,8 @@ struct Params {
   const float* sx;       // per-channel FP8: f32 scale per token row [RM] (or null)
   const float* sw;       //                  f32 scale per weight row [RN]
   int splits;            // K ranges per tile (split-K), else 1
+  int tile_base;         // logical tile of this launch's first workgroup (tile_coords order)
+  int part_tiles;        // split-K: tiles in this launch (partial tiles are numbered from 0)
   int M, N, K;
   int tiles_m, tiles_n;
 };
@@ -939,7 +944,7 @@ __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Bi
 }
 
 // Split-K output: the wave's fp32 accumulators as they sit in registers,
-// for mx_linear_slab_splitk's reduction. Partial tile (ks, tile) holds 65536
+// for the split-K reduction. Partial tile (ks, tile) holds 65536
 // floats; 16-byte chunk c = (((wave * 4 + i) * 4 + j) * 4 + q) * 64 + lane is
 // acc[i][j][4q .. 4q+3] of that lane: token m = m0 + 128 wm + 32 j + lane%32,
 // weight rows n = n0 + 128 wn + 32 i + 8 q + 4 (lane/32) + 0..3. One store
@@ -947,7 +952,7 @@ __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Bi
 // not written (the reduction skips them).
 __device__ __forceinline__ void store_tile_part(const f32x16 (&acc)[4][4], const Params& p, int tile, int ks, int m0,
                                                 int wave, int wm, int lane) {
-  float* base = p.part + ((size_t)ks * p.tiles_m * p.tiles_n + tile) * 65536;
+  float* base = p.part + ((size_t)ks * p.part_tiles + tile) * 65536;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(base, 65536u * 4u);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -983,9 +988,9 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   int bid = blockIdx.x, ks = 0;
   if constexpr (OUT == OUT_PART) {
     ks = bid % p.splits;
-    bid /= p.splits;
+    bid /= p.splits;  // the partial tile, numbered within this launch
   }
-  tile_coords(bid, p.tiles_m, p.tiles_n, tm, tn);
+  tile_coords(p.tile_base + bid, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_m = min(p.M - m0, BM);
   const int rows_n = min(p.N - n0, BN);
@@ -1055,7 +1060,7 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   if constexpr (OUT == OUT_Q)
     store_tile_q<EPI>(acc, B, p, smem + wave * 32768, m0, n0, wn, wm, lane);
   else if constexpr (OUT == OUT_PART)
-    store_tile_part(acc, p, tm * p.tiles_n + tn, ks, m0, wave, wm, lane);
+    store_tile_part(acc, p, bid, ks, m0, wave, wm, lane);
   else
     pp::store_tile8<EPI, 4, PC>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane,
                                 (const float*)(smem + PC_TABLE));
@@ -1068,12 +1073,13 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(Params p) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t tiles = p.part_tiles;
   if (u >= tiles * 16384) return;
   const int lane = (int)(u & 63), q = (int)(u >> 6) & 3, j = (int)(u >> 8) & 3, i = (int)(u >> 10) & 3;
   const int wave = (int)(u >> 12) & 3;
   const int tile = (int)(u >> 14);
-  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  int tm, tn;
+  tile_coords(p.tile_base + tile, p.tiles_m, p.tiles_n, tm, tn);
   const int m = tm * BM + (wave >> 1) * 128 + 32 * j + (lane & 31);
   const int n = tn * BN + (wave & 1) * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
   if (m >= p.M || n >= p.N) return;
@@ -1110,6 +1116,19 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
     configured = true;
   }
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(NT4), lds, st, p);
+  return hipGetLastError();
+}
+
+// Split-K over the launch's p.part_tiles tiles (from logical tile
+// p.tile_base): partial sums, then the ordered reduction.
+hipError_t launch_split(const Params& p, int epi, hipStream_t stream) {
+  hipError_t e = launch<0, OUT_PART>(p, p.part_tiles * p.splits, stream);
+  if (e != hipSuccess) return e;
+  const int nred = (int)(((int64_t)p.part_tiles * 16384 + 255) / 256);
+  if (epi == 1)
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3(nred), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3(nred), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1153,6 +1172,8 @@ hipError_t launch_linear(const void* x, const uint8_t* xs, int64_t M, int64_t K,
   p.sx = nullptr;
   p.sw = nullptr;
   p.splits = 1;
+  p.tile_base = 0;
+  p.part_tiles = 0;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -1181,6 +1202,8 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
   p.sx = nullptr;
   p.sw = nullptr;
   p.splits = 1;
+  p.tile_base = 0;
+  p.part_tiles = 0;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -1206,6 +1229,8 @@ hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int6
   p.sx = nullptr;
   p.sw = nullptr;
   p.splits = 1;
+  p.tile_base = 0;
+  p.part_tiles = 0;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -1236,15 +1261,62 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
   p.K = (int)K;
   p.tiles_m = (int)((M + BM - 1) / BM);
   p.tiles_n = (int)((N + BN - 1) / BN);
+  p.tile_base = 0;
+  p.part_tiles = p.tiles_m * p.tiles_n;
+  return slab::launch_split(p, epi, stream);
+}
+
+int64_t balanced_plan(int64_t M, int64_t K, int64_t N, int ncu, int64_t* full, int* splits) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t tail = tiles % ncu;
+  int64_t s = tail > 0 ? ncu / tail : 1;
+  s = std::min<int64_t>(s, kMaxTailSplits);
+  s = std::min<int64_t>(s, (K / 64) / 2);
+  if (s < 2) {  // nothing to balance: every tile data-parallel
+    *full = tiles;
+    *splits = 1;
+    return 0;
+  }
+  *full = tiles - tail;
+  *splits = (int)s;
+  return s * tail * 65536 * 4;
+}
+
+hipError_t launch_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                       const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int ncu,
+                                       float* part, hipStream_t stream) {
+  int64_t full;
+  int splits;
+  balanced_plan(M, K, N, ncu, &full, &splits);
+  Params p;
+  p.x = xq;
+  p.xs = xs;
+  p.wq = wq;
+  p.ws = ws;
+  p.bias = (const uint16_t*)bias;
+  p.y = (uint16_t*)y;
+  p.hq = nullptr;
+  p.hs = nullptr;
+  p.part = part;
+  p.sx = nullptr;
+  p.sw = nullptr;
+  p.splits = 1;
+  p.tile_base = 0;
+  p.part_tiles = 0;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-  hipError_t e = slab::launch<0, slab::OUT_PART>(p, (int)(tiles * splits), stream);
-  if (e != hipSuccess) return e;
-  const int nred = (int)((tiles * 16384 + 255) / 256);
-  if (epi == 1)
-    hipLaunchKernelGGL(slab::splitk_reduce_kernel<1>, dim3(nred), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(slab::splitk_reduce_kernel<0>, dim3(nred), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (full > 0) {
+    hipError_t e = epi == 1 ? slab::launch<1>(p, (int)full, stream) : slab::launch<0>(p, (int)full, stream);
+    if (e != hipSuccess || full == tiles) return e;
+  }
+  p.splits = splits;
+  p.tile_base = (int)full;
+  p.part_tiles = (int)(tiles - full);
+  return slab::launch_split(p, epi, stream);
 }
 
 hipError_t launch_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
@@ -1262,6 +1334,8 @@ hipError_t launch_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, 
   p.sx = xs;
   p.sw = ws;
   p.splits = 1;
+  p.tile_base = 0;
+  p.part_tiles = 0;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;

@@ -53,6 +53,15 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
                                      const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
                                      float* part, hipStream_t stream);
 
+// Balanced slab GEMM: the full rounds of ncu tiles data-parallel, the last,
+// partial round split over K (at most 8 ranges, at least 2 slabs each) with
+// fp32 partials in `part`. balanced_plan gives the number of data-parallel
+// tiles, the split count (1: no split) and the partial bytes needed.
+int64_t balanced_plan(int64_t M, int64_t K, int64_t N, int ncu, int64_t* full, int* splits);
+hipError_t launch_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                       const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int ncu,
+                                       float* part, hipStream_t stream);
+
 // Per-output-channel FP8: rows of x (bf16, kind 0, or f32, kind 1; pitch ld)
 // to E4M3 codes in the slab layout q [K/64][R][64] and one f32 scale per row
 // s [R] (R = slab_rows(rows); pad rows zero). K % 64 == 0.

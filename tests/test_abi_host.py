@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 6
+    assert L.mx_abi_version() == 7
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -208,6 +208,34 @@ def test_splitk_rejects_bad_arguments(L):
     assert call(epi=7) == 1
     assert call(N=264) == 2
     assert call(M=0) == 0 and call(N=0) == 0
+
+
+def test_balanced_plan_sizes(L):
+    # No GPU here: the plan assumes 256 compute units (MI355X).
+    KB256 = 65536 * 4
+    assert L.mx_linear_balanced_ws_bytes(75348, 5120, 5120) == 8 * 12 * KB256  # 5900 tiles: 12 in the last round
+    assert L.mx_linear_balanced_ws_bytes(75348, 5120, 15360) == 7 * 36 * KB256  # 17700 tiles: 36, 256 // 36 = 7
+    assert L.mx_linear_balanced_ws_bytes(128, 5120, 5120) == 8 * 20 * KB256  # 20 tiles, all split
+    assert L.mx_linear_balanced_ws_bytes(256 * 16, 512, 256 * 16) == 0  # 256 tiles: whole rounds
+    assert L.mx_linear_balanced_ws_bytes(300, 128, 256) == 0  # K/128 = 1: nothing to split
+    assert L.mx_linear_balanced_ws_bytes(0, 64, 16) == 0
+    assert L.mx_linear_balanced_ws_bytes(8, 96, 16) == -1 and L.mx_linear_balanced_ws_bytes(-1, 64, 16) == -1
+
+
+def test_balanced_rejects_bad_arguments(L):
+    f = L.mx_linear_slab_balanced
+    need = L.mx_linear_balanced_ws_bytes(8, 256, 256)
+    assert need > 0
+    E = 0x50000000
+
+    def call(xq=A, xs=B, M=8, K=256, wq=C, ws=C + (1 << 20), N=256, epi=0, y=D, wsp=E, nb=need):
+        return f(P(xq), P(xs), M, K, P(wq), P(ws), N, P(0), epi, P(y), P(wsp), nb, P(0))
+
+    assert call(K=96) == 1 and call(epi=3) == 1 and call(y=0) == 1
+    assert call(nb=need - 1) == 1 and call(wsp=0) == 1 and call(wsp=E + 16) == 1
+    assert call(wsp=A) == 1 and call(y=E) == 1
+    assert call(N=264) == 2
+    assert call(M=0) == 0
 
 
 def test_pc_calls_reject_bad_arguments(L):

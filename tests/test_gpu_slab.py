@@ -353,3 +353,80 @@ def test_splitk_small_token_configs(cfg):
     torch.cuda.synchronize()
     yref, S = oracle_linear(x, w, b, shp.gelu)
     assert_linear_close(y, yref, S, "gelu_tanh" if shp.gelu else "none", what=cfg)
+
+
+def tile_coords(pid, tiles_m, tiles_n, gm=4):
+    """The kernels' workgroup -> (token tile, weight tile) order: XCD ranges,
+    then groups of 4 token tiles x all weight tiles."""
+    nwg = tiles_m * tiles_n
+    q, r = nwg >> 3, nwg & 7
+    xcd, k = pid & 7, pid >> 3
+    lid = xcd * q + min(xcd, r) + k
+    group = lid // (gm * tiles_n)
+    first_m = group * gm
+    g = min(tiles_m - first_m, gm)
+    in_group = lid - group * gm * tiles_n
+    return first_m + in_group % g, in_group // g
+
+
+def split_tile_mask(M, N, ncu=256):
+    tm_, tn_ = (M + 255) // 256, (N + 255) // 256
+    tiles = tm_ * tn_
+    mask = np.zeros((M, N), dtype=bool)
+    for pid in range(tiles - tiles % ncu, tiles):
+        a, b = tile_coords(pid, tm_, tn_)
+        mask[a * 256:(a + 1) * 256, b * 256:(b + 1) * 256] = True
+    return mask
+
+
+def test_tile_order_is_a_bijection():
+    for tm_, tn_ in ((1, 20), (295, 20), (295, 60), (17, 16), (3, 5)):
+        seen = {tile_coords(p, tm_, tn_) for p in range(tm_ * tn_)}
+        assert seen == {(a, b) for a in range(tm_) for b in range(tn_)}
+
+
+@pytest.mark.parametrize("M,K,N,gelu", [(4352, 512, 4096, False), (300, 256, 512, True), (128, 5120, 5120, False)])
+def test_balanced_matches_slab_and_oracle(M, K, N, gelu):
+    # Tiles of the full rounds equal mx_linear_slab bit for bit; the split
+    # last round (and everything) is within the tolerance of the oracle.
+    print(f"balanced M={M} K={K} N={N}", flush=True)
+    d = dev()
+    x = synth.make_activation(M, K, seed=M + N + 1)
+    w = synth.make_weight(N, K, seed=M + N + 1)
+    b = synth.make_bias(N, seed=M + N + 1)
+    xs = mx().mx_quantize_act_slab(x.to(d))
+    ws = mx().mx_quantize_weight_slab(w.to(d))
+    y1 = mx().mx_linear_slab(xs, ws, b.to(d), gelu=gelu)
+    y2 = mx().mx_linear_slab_balanced(xs, ws, b.to(d), gelu=gelu)
+    y3 = mx().mx_linear_slab_balanced(xs, ws, b.to(d), gelu=gelu)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
+    props = torch.cuda.get_device_properties(d)
+    mask = torch.from_numpy(split_tile_mask(M, N, props.multi_processor_count))
+    if mx().mx_linear_balanced_ws_bytes(M, K, N) == 0:
+        mask[:] = False
+    keep = ~mask.to(d)
+    assert torch.equal(y1.view(torch.int16)[keep], y2.view(torch.int16)[keep])
+    yref, S = oracle_linear(x, w, b, gelu)
+    assert_linear_close(y2, yref, S, "gelu_tanh" if gelu else "none", what="balanced")
+
+
+def test_balanced_full_size_n5120():
+    # 75348 x 5120 x 5120: 5900 tiles, the last 12 split; sampled rows of the
+    # split tiles against the oracle, the rest bit-identical to the plain GEMM.
+    d = dev()
+    M, K, N = synth.VIDEO_TOKENS, synth.HIDDEN, synth.HIDDEN
+    x = synth.make_activation(M, K, 41)
+    w, b = synth.make_weight(N, K, 41), synth.make_bias(N, 41)
+    xs = mx().mx_quantize_act_slab(x.to(d))
+    ws = mx().mx_quantize_weight_slab(w.to(d))
+    y1 = mx().mx_linear_slab(xs, ws, b.to(d))
+    y2 = mx().mx_linear_slab_balanced(xs, ws, b.to(d))
+    torch.cuda.synchronize()
+    props = torch.cuda.get_device_properties(d)
+    mask = split_tile_mask(M, N, props.multi_processor_count)
+    keep = torch.from_numpy(~mask).to(d)
+    assert torch.equal(y1.view(torch.int16)[keep], y2.view(torch.int16)[keep])
+    rows = np.unique(np.nonzero(mask.any(axis=1))[0][::97])
+    yref, S = oracle.linear_ref(*quant_ref(x[rows]), *quant_ref(w), bias=f64(b))
+    assert_linear_close(y2[rows], yref, S, what="balanced full size")
