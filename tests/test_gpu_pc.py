@@ -178,3 +178,29 @@ def test_pc_quantizer_quotients_at_rounding_ties():
     sl = mx().mx_pc_quantize_act_slab(xb.to(dev()))
     torch.cuda.synchronize()
     check_quant(sl, xb.float().numpy())
+
+
+def test_pc_offsets_past_4gib():
+    # As the MX path's test: 2^20 + 77 rows of a repeated seeded block, the
+    # per-channel code slab past 2^32 bytes; codes, scales and outputs of
+    # sampled rows against the oracle.
+    d = dev()
+    M, K, N = (1 << 20) + 77, 5120, 256
+    base = synth.make_activation(1000, K, seed=62)
+    w, b = synth.make_weight(N, K, 62), synth.make_bias(N, 62)
+    x = base.to(d).repeat((M + 999) // 1000, 1)[:M]
+    xs = mx().mx_pc_quantize_act_slab(x)
+    assert xs.q.numel() > 1 << 32
+    ws = mx().mx_pc_quantize_weight_slab(w.to(d))
+    y = mx().mx_pc_linear_slab(xs, ws, b.to(d))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([np.arange(3), np.arange(M - 80, M), rng.integers(0, M, 64),
+                                     [(1 << 32) // K, (1 << 32) // K + 1]]))
+    q, s = rows_of(xs, torch.from_numpy(rows))
+    rq, rs = oracle.quantize_pc(base[rows % 1000].float().numpy())
+    assert np.array_equal(q, rq) and same_f32(s, rs)
+    yref, S = oracle_pc(base[rows % 1000], w, b, False)
+    assert_linear_close(y[rows], yref, S, what="pc offsets past 4 GiB")
+    del x, xs, y
+    torch.cuda.empty_cache()

@@ -430,3 +430,28 @@ def test_balanced_full_size_n5120():
     rows = np.unique(np.nonzero(mask.any(axis=1))[0][::97])
     yref, S = oracle.linear_ref(*quant_ref(x[rows]), *quant_ref(w), bias=f64(b))
     assert_linear_close(y2[rows], yref, S, what="balanced full size")
+
+
+def test_linear_ws_offsets_past_4gib():
+    # 2^20 + 77 token rows at K = 5120: the activation slab is 5.4 GB, so the
+    # quantizer takes its 64-bit index path and the GEMM's slab offsets pass
+    # 2^32 bytes. The rows are a seeded block of 1000 rows repeated, so the
+    # oracle knows every row; sampled rows across the whole range, the last
+    # (ragged) tile included, are checked.
+    d = dev()
+    M, K, N = (1 << 20) + 77, 5120, 256
+    base = synth.make_activation(1000, K, seed=61)
+    w, b = synth.make_weight(N, K, 61), synth.make_bias(N, 61)
+    x = base.to(d).repeat((M + 999) // 1000, 1)[:M]
+    wsl = mx().mx_quantize_weight_slab(w.to(d))
+    ws = torch.empty((mx().mx_linear_ws_bytes(M, K),), dtype=torch.uint8, device=d)
+    assert ws.numel() > 1 << 32
+    y = mx().mx_linear_ws(x, wsl, b.to(d), workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([np.arange(3), np.arange(M - 80, M), rng.integers(0, M, 64),
+                                     [(1 << 31) // K, (1 << 32) // K, (1 << 32) // K + 1]]))
+    yref, S = oracle_linear(base[rows % 1000], w, b, False)
+    assert_linear_close(y[rows], yref, S, what="offsets past 4 GiB")
+    del x, ws, y
+    torch.cuda.empty_cache()
