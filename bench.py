@@ -185,20 +185,18 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
         outs = [torch.empty((shp.M, shp.N), dtype=torch.bfloat16, device=dev) for shp, _, _ in layers]
         slabs = [mx.mx_quantize_act_slab(acts[li] if acts[li] is not None else outs[li - 1])
                  for li in range(len(layers))]
-        # Few token tiles: split-K (partial sums in a workspace, ordered reduction).
-        splits = [mx.mx_linear_splitk_choose(shp.M, shp.K, shp.N) for shp, _, _ in layers]
-        wss = [torch.empty((mx.mx_linear_splitk_ws_bytes(shp.M, shp.N, sp),), dtype=torch.uint8, device=dev)
-               if sp > 1 else None for (shp, _, _), sp in zip(layers, splits)]
+        # Per-shape kernel: the few-token kernel up to 256 tokens, split-K
+        # (partial sums in a workspace, ordered reduction) when the 256 x 256
+        # tiles leave CUs idle, else the slab GEMM.
+        plans = [mx.plan_linear(shp.M, shp.K, shp.N) for shp, _, _ in layers]
+        wss = [torch.empty((mx.plan_ws_bytes(pl, shp.M, shp.N),), dtype=torch.uint8, device=dev)
+               if mx.plan_ws_bytes(pl, shp.M, shp.N) > 0 else None for (shp, _, _), pl in zip(layers, plans)]
 
         def run():
             for li, (shp, w, b) in enumerate(layers):
                 x = acts[li] if acts[li] is not None else outs[li - 1]
                 mx.mx_quantize_act_slab(x, slabs[li])
-                if splits[li] > 1:
-                    mx.mx_linear_slab_splitk(slabs[li], w, b, gelu=shp.gelu, y=outs[li], splits=splits[li],
-                                             workspace=wss[li])
-                else:
-                    mx.mx_linear_slab(slabs[li], w, b, gelu=shp.gelu, y=outs[li])
+                mx.mx_linear_slab_planned(plans[li], slabs[li], w, b, gelu=shp.gelu, y=outs[li], workspace=wss[li])
 
         total, _ = timed_step(torch, [run], steps, warmup)
         ms = total / steps
@@ -206,7 +204,7 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
         flop = sum(2.0 * shp.M * shp.N * shp.K for shp, _, _ in layers)
         res[name] = {
             "linears": [f"{shp.name} {shp.M}x{shp.K}x{shp.N}" + (" gelu" if shp.gelu else "")
-                        + (f" splitk{sp}" if sp > 1 else "") for (shp, _, _), sp in zip(layers, splits)],
+                        + ("" if pl[0] == "slab" else f" {pl[0]}{pl[1]}") for (shp, _, _), pl in zip(layers, plans)],
             "ms": round(ms, 4),
             "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
             "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),

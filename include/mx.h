@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 7
+#define MX_ABI_VERSION 8
 
 typedef enum {
   MX_OK = 0,
@@ -217,6 +217,39 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
                           const uint8_t* wq, const uint8_t* ws, int64_t N,
                           const void* bias, int epilogue, void* y, int splits,
                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Few-token tiles. For M up to a few hundred the result is computed by a
+ * kernel with 128-token x 64-weight-row tiles (four waves of 32 tokens), which
+ * streams each weight row once per K range while the token slab stays in
+ * the L2, instead of padding the tokens to 256. K is split into `splits`
+ * ranges: splits = 1 writes y directly, bit-identical to mx_linear_slab (the
+ * same chain of MFMAs in K order, the same epilogue); splits > 1 writes fp32
+ * partials [splits][M][N] that a second kernel adds in range order before
+ * bias, epilogue and bf16: fixed order, deterministic, the tolerance of
+ * mx_linear_slab. */
+
+/* Workspace bytes for mx_linear_slab_small: splits * M * N * 4 when
+ * splits > 1, else 0; -1 on bad arguments. */
+int64_t mx_linear_small_ws_bytes(int64_t M, int64_t N, int splits);
+
+/* A split count for mx_linear_slab_small on the current device: about one
+ * workgroup per CU (C / ceil(M/128) / ceil(N/64)), at most 8 ranges and at
+ * least two 64-K slabs per range; 1 when the tiles alone fill the CUs or on
+ * bad arguments. */
+int mx_linear_small_choose(int64_t M, int64_t K, int64_t N);
+
+/* mx_linear_slab through the few-token kernel (operands, bias, epilogue, y
+ * and their errors as there). 1 <= splits <= K/64 (else
+ * MX_ERR_INVALID_ARGUMENT); ceil(M/128) * ceil(N/64) * splits <= 2^24 and
+ * (K/64 + 16) * 64 * R < 2^31 for R = M and N rounded up to 256 (else
+ * MX_ERR_UNSUPPORTED). workspace: at least mx_linear_small_ws_bytes(M, N,
+ * splits) bytes, 256-byte aligned, not overlapping an operand, bias or y; may
+ * be NULL when that is 0; overwritten. One or two kernels on `stream`;
+ * nothing is allocated. */
+int mx_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                         const uint8_t* wq, const uint8_t* ws, int64_t N,
+                         const void* bias, int epilogue, void* y, int splits,
+                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes mx_linear_slab_balanced needs on the current device: the
  * fp32 partial tiles of its split last round, 0 when it splits nothing; -1 on

@@ -48,6 +48,9 @@ SIGNATURES = {
     "mx_linear_splitk_ws_bytes": ([_I64, _I64, _INT], _I64),
     "mx_linear_splitk_choose": ([_I64, _I64, _I64], _INT),
     "mx_linear_slab_splitk": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
+    "mx_linear_small_ws_bytes": ([_I64, _I64, _INT], _I64),
+    "mx_linear_small_choose": ([_I64, _I64, _I64], _INT),
+    "mx_linear_slab_small": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
     "mx_linear_balanced_ws_bytes": ([_I64, _I64, _I64], _I64),
     "mx_linear_slab_balanced": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
@@ -413,6 +416,77 @@ def mx_linear_slab_splitk(x, w, bias=None, gelu=False, y=None, splits=None, work
             )
         )
     return y
+
+
+def mx_linear_small_ws_bytes(M, N, splits):
+    return lib().mx_linear_small_ws_bytes(M, N, splits)
+
+
+def mx_linear_small_choose(M, K, N):
+    return lib().mx_linear_small_choose(M, K, N)
+
+
+def mx_linear_slab_small(x, w, bias=None, gelu=False, y=None, splits=None, workspace=None):
+    """mx_linear_slab through the few-token kernel (128 x 64 tiles) with
+    `splits` K ranges (default mx_linear_small_choose); workspace: uint8 of
+    at least mx_linear_small_ws_bytes(M, N, splits) bytes (allocated here
+    when None and needed)."""
+    dev, M, N, K = _slab_linear_args(x, w, bias)
+    splits = mx_linear_small_choose(M, K, N) if splits is None else int(splits)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    need = mx_linear_small_ws_bytes(M, N, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear_slab_small(
+                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), splits,
+                _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev),
+            )
+        )
+    return y
+
+
+# Few-token kernel up to this many tokens; measured on MI355X at K = 5120 it
+# beats split-K on 256 x 256 tiles for M = 128 and 256 (16.0 vs 20.4 us,
+# 19.1 vs 25.7 us) and loses from M = 512 (54.8 vs 47.7 us at N = 10240).
+SMALL_MAX_TOKENS = 256
+
+
+def plan_linear(M, K, N):
+    """Kernel for an M x K x N slab linear: ("small", splits) for at most
+    SMALL_MAX_TOKENS tokens, else ("splitk", splits) when the 256 x 256 tiles
+    leave CUs idle, else ("slab", 1)."""
+    if 0 < M <= SMALL_MAX_TOKENS:
+        return "small", mx_linear_small_choose(M, K, N)
+    sp = mx_linear_splitk_choose(M, K, N)
+    return ("splitk", sp) if sp > 1 else ("slab", 1)
+
+
+def plan_ws_bytes(plan, M, N):
+    """Workspace bytes of a plan from plan_linear (0 when none is needed)."""
+    kind, sp = plan
+    if kind == "small":
+        return mx_linear_small_ws_bytes(M, N, sp)
+    if kind == "splitk":
+        return mx_linear_splitk_ws_bytes(M, N, sp)
+    return 0
+
+
+def mx_linear_slab_planned(plan, x, w, bias=None, gelu=False, y=None, workspace=None):
+    """mx_linear_slab through the kernel a plan_linear plan names."""
+    kind, sp = plan
+    if kind == "small":
+        return mx_linear_slab_small(x, w, bias, gelu=gelu, y=y, splits=sp, workspace=workspace)
+    if kind == "splitk":
+        return mx_linear_slab_splitk(x, w, bias, gelu=gelu, y=y, splits=sp, workspace=workspace)
+    return mx_linear_slab(x, w, bias, gelu=gelu, y=y)
 
 
 def mx_linear_balanced_ws_bytes(M, K, N):

@@ -417,6 +417,58 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
                 "linear launch");
 }
 
+int64_t mx_linear_small_ws_bytes(int64_t M, int64_t N, int splits) {
+  if (M < 0 || N < 0 || M > kMaxRows || N > kMaxKN || splits < 1 || splits > kMaxKN / 64) return -1;
+  return splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+}
+
+int mx_linear_small_choose(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || N <= 0 || K < 64 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN) return 1;
+  int64_t s = cu_count() / mx::small_tiles(M, N);  // about one workgroup per CU
+  s = std::min<int64_t>(s, kMaxAutoSplits);         // partial-sum traffic grows with the split count
+  s = std::min<int64_t>(s, K / 128);                // at least two 64-K slabs per range
+  return (int)std::max<int64_t>(s, 1);
+}
+
+int mx_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                         const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y, int splits,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK) return st;
+  if (splits < 1 || splits > K / 64)
+    return fail(MX_ERR_INVALID_ARGUMENT, "splits = %d must be in [1, K/64 = %lld]", splits, (long long)(K / 64));
+  if (M == 0 || N == 0) return MX_OK;
+  if (y == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL y");
+  if (!aligned(y, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned");
+  // The kernel addresses a tile's K range with 32-bit offsets that run a few
+  // slabs past it.
+  const int64_t span = K / 64 + 16;
+  if (span * mx::slab_rows(M) * 64 >= (int64_t(1) << 31) || span * mx::slab_rows(N) * 64 >= (int64_t(1) << 31))
+    return fail(MX_ERR_UNSUPPORTED, "(K/64 + 16) * 64 * rows must be below 2^31 for M and N (M = %lld, N = %lld)",
+                (long long)M, (long long)N);
+  const int64_t tiles = mx::small_tiles(M, N);
+  if (tiles * splits > kMaxSplitWorkgroups)
+    return fail(MX_ERR_UNSUPPORTED, "%lld tiles x %d splits exceed 2^24 workgroups", (long long)tiles, splits);
+  const int64_t need = mx_linear_small_ws_bytes(M, N, splits);
+  const uint64_t ybytes = (uint64_t)M * N * 2;
+  if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, y, ybytes, "y")) != MX_OK) return st;
+  if (need > 0) {
+    if (workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL workspace (%lld bytes needed)", (long long)need);
+    if (!aligned(workspace, 256)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)need);
+    if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, workspace, (uint64_t)need, "workspace")) != MX_OK)
+      return st;
+    if (overlap(workspace, (uint64_t)need, y, ybytes)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps y");
+  }
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_linear_slab_small(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, (float*)workspace,
+                                             (hipStream_t)stream),
+                "linear launch");
+}
+
 int mx_pc_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, float* s, void* stream) {
   const int st = check_pc_quantize(x, MX_DT_BF16, M, K, ldx, q, s);
   if (st != MX_OK || M == 0) return st;

@@ -53,6 +53,15 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
                                      const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
                                      float* part, hipStream_t stream);
 
+// Few-token slab GEMM (128-token x 64-weight-row tiles, see mx_small.hip):
+// splits == 1 writes y directly; splits > 1 writes f32 partials [splits][M][N]
+// into `part` and reduces them in range order. small_tiles gives the tile
+// count. 1 <= splits <= K/64, N % 16 == 0.
+int64_t small_tiles(int64_t M, int64_t N);
+hipError_t launch_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                    const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
+                                    float* part, hipStream_t stream);
+
 // Balanced slab GEMM: the full rounds of ncu tiles data-parallel, the last,
 // partial round split over K (at most 8 ranges, at least 2 slabs each) with
 // fp32 partials in `part`. balanced_plan gives the number of data-parallel

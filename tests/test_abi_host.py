@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 7
+    assert L.mx_abi_version() == 8
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -210,6 +210,39 @@ def test_splitk_rejects_bad_arguments(L):
     assert call(M=0) == 0 and call(N=0) == 0
 
 
+def test_small_sizes_and_choice(L):
+    # No GPU here: the choice assumes 256 compute units (MI355X).
+    assert L.mx_linear_small_ws_bytes(128, 5120, 3) == 3 * 128 * 5120 * 4  # fp32 partials [splits][M][N]
+    assert L.mx_linear_small_ws_bytes(128, 5120, 1) == 0  # one range writes y directly
+    assert L.mx_linear_small_ws_bytes(1, 16, 0) == -1 and L.mx_linear_small_ws_bytes(-1, 16, 2) == -1
+    assert L.mx_linear_small_choose(128, 5120, 5120) == 3  # 80 tiles of 128 x 64
+    assert L.mx_linear_small_choose(512, 5120, 10240) == 1  # 640 tiles fill the CUs
+    assert L.mx_linear_small_choose(1, 256, 256) == 2  # 4 tiles; K/64 = 4 slabs: two per range
+    assert L.mx_linear_small_choose(1, 64, 256) == 1
+    assert L.mx_linear_small_choose(1, 5120, 64) == 8  # capped at 8
+    assert L.mx_linear_small_choose(0, 64, 256) == 1
+
+
+def test_small_rejects_bad_arguments(L):
+    f = L.mx_linear_slab_small
+    need = L.mx_linear_small_ws_bytes(8, 256, 2)
+    E = 0x50000000
+
+    def call(xq=A, xs=B, M=8, K=256, wq=C, ws=C + (1 << 20), N=256, epi=0, y=D, splits=2, wsp=E, nb=need):
+        return f(P(xq), P(xs), M, K, P(wq), P(ws), N, P(0), epi, P(y), splits, P(wsp), nb, P(0))
+
+    assert call(splits=0) == 1 and call(splits=5) == 1  # outside [1, K/64]
+    assert call(K=96) == 1  # K % 64
+    assert call(nb=need - 1) == 1
+    assert call(wsp=0) == 1 and call(y=0) == 1 and call(xq=0) == 1
+    assert call(wsp=E + 16) == 1
+    assert call(wsp=A) == 1  # workspace overlaps the token codes
+    assert call(y=E) == 1  # y overlaps the workspace
+    assert call(epi=7) == 1
+    assert call(N=264) == 2
+    assert call(M=0) == 0 and call(N=0) == 0
+
+
 def test_balanced_plan_sizes(L):
     # No GPU here: the plan assumes 256 compute units (MI355X).
     KB256 = 65536 * 4
@@ -281,3 +314,17 @@ def test_oracle_and_product_share_no_code():
             text = open(os.path.join(ROOT, "oracle", fn)).read()
             assert "mxfp8_w8a8_quantized_amd" not in text, fn
             assert "synth" not in text, fn
+
+
+def test_per_shape_plan():
+    # No GPU here: the split choices assume 256 compute units (MI355X).
+    import mxfp8_w8a8_quantized_amd as pkg
+
+    assert pkg.plan_linear(128, 5120, 5120) == ("small", 3)
+    assert pkg.plan_linear(256, 5120, 5120) == ("small", 1)
+    assert pkg.plan_linear(512, 5120, 10240) == ("splitk", 3)
+    assert pkg.plan_linear(75348, 5120, 15360) == ("slab", 1)
+    assert pkg.plan_ws_bytes(("small", 3), 128, 5120) == 3 * 128 * 5120 * 4
+    assert pkg.plan_ws_bytes(("small", 1), 128, 5120) == 0
+    assert pkg.plan_ws_bytes(("splitk", 3), 512, 10240) == 3 * 2 * 40 * 65536 * 4
+    assert pkg.plan_ws_bytes(("slab", 1), 75348, 15360) == 0
