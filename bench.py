@@ -185,12 +185,14 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
         outs = [torch.empty((shp.M, shp.N), dtype=torch.bfloat16, device=dev) for shp, _, _ in layers]
         slabs = [mx.mx_quantize_act_slab(acts[li] if acts[li] is not None else outs[li - 1])
                  for li in range(len(layers))]
-        # Per-shape kernel: the few-token kernel up to 256 tokens, split-K
-        # (partial sums in a workspace, ordered reduction) when the 256 x 256
-        # tiles leave CUs idle, else the slab GEMM.
+        # Per-shape kernel: the default plan (few-token kernel up to 256
+        # tokens, split-K while the 256 x 256 tiles leave CUs idle, else the
+        # slab GEMM), then warm-up tuning on the real operands of each linear
+        # (mx_linear_tune times the candidate kernels and caches the fastest);
+        # the timed step runs the tuned plans.
         plans = [mx.plan_linear(shp.M, shp.K, shp.N) for shp, _, _ in layers]
-        wss = [torch.empty((mx.plan_ws_bytes(pl, shp.M, shp.N),), dtype=torch.uint8, device=dev)
-               if mx.plan_ws_bytes(pl, shp.M, shp.N) > 0 else None for (shp, _, _), pl in zip(layers, plans)]
+        wss = [torch.empty((max(mx.mx_linear_tune_ws_bytes(shp.M, shp.K, shp.N), 1),), dtype=torch.uint8, device=dev)
+               for shp, _, _ in layers]
 
         def run():
             for li, (shp, w, b) in enumerate(layers):
@@ -198,13 +200,22 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
                 mx.mx_quantize_act_slab(x, slabs[li])
                 mx.mx_linear_slab_planned(plans[li], slabs[li], w, b, gelu=shp.gelu, y=outs[li], workspace=wss[li])
 
+        run()
+        default_plans = list(plans)
+        for li, (shp, w, b) in enumerate(layers):
+            if shp.M <= 4096:  # the large shapes' plan is the slab GEMM; tuning them takes seconds
+                plans[li] = mx.mx_linear_tune(slabs[li], w, b, gelu=shp.gelu, y=outs[li], workspace=wss[li], reps=5)
+        run()
+
         total, _ = timed_step(torch, [run], steps, warmup)
         ms = total / steps
         g_ms = graph_ms(torch, run, steps)
         flop = sum(2.0 * shp.M * shp.N * shp.K for shp, _, _ in layers)
         res[name] = {
             "linears": [f"{shp.name} {shp.M}x{shp.K}x{shp.N}" + (" gelu" if shp.gelu else "")
-                        + ("" if pl[0] == "slab" else f" {pl[0]}{pl[1]}") for (shp, _, _), pl in zip(layers, plans)],
+                        + ("" if pl[0] == "slab" else f" {pl[0]}{pl[1]}")
+                        + ("" if pl == d else f" (tuned; default {d[0]}{d[1]})")
+                        for (shp, _, _), pl, d in zip(layers, plans, default_plans)],
             "ms": round(ms, 4),
             "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
             "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 8
+#define MX_ABI_VERSION 9
 
 typedef enum {
   MX_OK = 0,
@@ -250,6 +250,73 @@ int mx_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_
                          const uint8_t* wq, const uint8_t* ws, int64_t N,
                          const void* bias, int epilogue, void* y, int splits,
                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-shape plans. A plan names the kernel for one slab-linear shape and its
+ * K split: MX_PLAN_SLAB (mx_linear_slab, splits 1), MX_PLAN_SPLITK
+ * (mx_linear_slab_splitk), MX_PLAN_SMALL (mx_linear_slab_small),
+ * MX_PLAN_BALANCED (mx_linear_slab_balanced, splits 1). Every plan computes
+ * the same linear (same operands, tolerance and determinism; SLAB, and SPLITK
+ * or SMALL with splits 1, bit-identical). The library keeps a process-local
+ * cache of tuned plans keyed by (device, M, K, N, epilogue), guarded by a
+ * mutex; mx_linear_tune fills it, mx_linear_slab_auto reads it.
+ * ------------------------------------------------------------------------ */
+enum { MX_PLAN_SLAB = 0, MX_PLAN_SPLITK = 1, MX_PLAN_SMALL = 2, MX_PLAN_BALANCED = 3 };
+
+/* The rule used without tuning: MX_PLAN_SMALL with mx_linear_small_choose
+ * splits for 1 <= M <= 256; else MX_PLAN_SPLITK with
+ * mx_linear_splitk_choose splits when that is above 1; else MX_PLAN_SLAB.
+ * MX_ERR_INVALID_ARGUMENT on NULL outputs or a bad shape (M, N < 0; K not a
+ * positive multiple of 64; sizes past the slab linear's limits). */
+int mx_linear_plan_default(int64_t M, int64_t K, int64_t N, int* kind, int* splits);
+
+/* Workspace bytes of a plan for this shape (0 when it needs none); -1 on a
+ * bad kind, split count or shape. */
+int64_t mx_linear_plan_ws_bytes(int kind, int splits, int64_t M, int64_t K, int64_t N);
+
+/* mx_linear_slab through the given plan: the arguments, checks and errors of
+ * that plan's entry point (workspace unused by MX_PLAN_SLAB). */
+int mx_linear_slab_plan(int kind, int splits, const uint8_t* xq, const uint8_t* xs,
+                        int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws,
+                        int64_t N, const void* bias, int epilogue, void* y,
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The largest workspace a candidate of mx_linear_tune uses for this shape
+ * (so also enough for the plan it picks); -1 on a bad shape. */
+int64_t mx_linear_tune_ws_bytes(int64_t M, int64_t K, int64_t N);
+
+/* Warm-up tuning of one shape on the caller's operands: runs each candidate
+ * plan once, then `reps` times between two HIP events on `stream` (1 <=
+ * reps <= 1000), and keeps the fastest. Candidates: the default plan; the
+ * slab GEMM; split-K with 2, 3, 4, 6, 8 ranges when the 256 x 256 tiles are
+ * fewer than the device's CUs; the few-token kernel with 1, 2, 3, 4, 6, 8
+ * ranges for M <= 1024; the balanced GEMM when the tiles leave a partial
+ * last round. Candidates whose workspace exceeds workspace_bytes, or that
+ * their entry point rejects, are skipped. The choice is cached for (current
+ * device, M, K, N, epilogue) and written to *kind, *splits. y is
+ * overwritten; the stream is synchronized (not for use under graph
+ * capture). Errors: those of the slab linear's checks, MX_ERR_INVALID_ARGUMENT
+ * when no candidate fits the workspace, MX_ERR_HIP from the runs. */
+int mx_linear_tune(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                   const uint8_t* wq, const uint8_t* ws, int64_t N,
+                   const void* bias, int epilogue, void* y,
+                   void* workspace, int64_t workspace_bytes, int reps, void* stream,
+                   int* kind, int* splits);
+
+/* The cached plan of (current device, M, K, N, epilogue) if tuned, else the
+ * default plan. */
+int mx_linear_plan_lookup(int64_t M, int64_t K, int64_t N, int epilogue, int* kind, int* splits);
+
+/* mx_linear_slab through mx_linear_plan_lookup's plan. workspace: at least
+ * mx_linear_plan_ws_bytes of that plan (mx_linear_tune_ws_bytes always
+ * suffices); may be NULL when the plan needs none. Nothing is allocated. */
+int mx_linear_slab_auto(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                        const uint8_t* wq, const uint8_t* ws, int64_t N,
+                        const void* bias, int epilogue, void* y,
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Empties the plan cache. */
+void mx_linear_plan_clear(void);
 
 /* Workspace bytes mx_linear_slab_balanced needs on the current device: the
  * fp32 partial tiles of its split last round, 0 when it splits nothing; -1 on

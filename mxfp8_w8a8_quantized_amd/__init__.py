@@ -23,11 +23,18 @@ MX_EPI_NONE = 0
 MX_EPI_GELU_TANH = 1
 MX_DT_BF16 = 0
 MX_DT_F32 = 1
+MX_PLAN_SLAB = 0
+MX_PLAN_SPLITK = 1
+MX_PLAN_SMALL = 2
+MX_PLAN_BALANCED = 3
+PLAN_NAMES = {MX_PLAN_SLAB: "slab", MX_PLAN_SPLITK: "splitk", MX_PLAN_SMALL: "small", MX_PLAN_BALANCED: "balanced"}
+PLAN_KINDS = {v: k for k, v in PLAN_NAMES.items()}
 
 # Every symbol include/mx.h declares, with its ctypes signature.
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
+_PI = ctypes.POINTER(ctypes.c_int)
 SIGNATURES = {
     "mx_abi_version": ([], _INT),
     "mx_status_string": ([_INT], ctypes.c_char_p),
@@ -53,6 +60,14 @@ SIGNATURES = {
     "mx_linear_slab_small": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
     "mx_linear_balanced_ws_bytes": ([_I64, _I64, _I64], _I64),
     "mx_linear_slab_balanced": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
+    "mx_linear_plan_default": ([_I64, _I64, _I64, _PI, _PI], _INT),
+    "mx_linear_plan_ws_bytes": ([_INT, _INT, _I64, _I64, _I64], _I64),
+    "mx_linear_slab_plan": ([_INT, _INT, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
+    "mx_linear_tune_ws_bytes": ([_I64, _I64, _I64], _I64),
+    "mx_linear_tune": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _INT, _P, _PI, _PI], _INT),
+    "mx_linear_plan_lookup": ([_I64, _I64, _I64, _INT, _PI, _PI], _INT),
+    "mx_linear_slab_auto": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
+    "mx_linear_plan_clear": ([], None),
     "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
@@ -453,40 +468,106 @@ def mx_linear_slab_small(x, w, bias=None, gelu=False, y=None, splits=None, works
     return y
 
 
-# Few-token kernel up to this many tokens; measured on MI355X at K = 5120 it
-# beats split-K on 256 x 256 tiles for M = 128 and 256 (16.0 vs 20.4 us,
-# 19.1 vs 25.7 us) and loses from M = 512 (54.8 vs 47.7 us at N = 10240).
-SMALL_MAX_TOKENS = 256
+def _plan_out(fn, *args):
+    kind, splits = ctypes.c_int(0), ctypes.c_int(0)
+    _check(fn(*args, ctypes.byref(kind), ctypes.byref(splits)))
+    return PLAN_NAMES[kind.value], splits.value
 
 
 def plan_linear(M, K, N):
-    """Kernel for an M x K x N slab linear: ("small", splits) for at most
-    SMALL_MAX_TOKENS tokens, else ("splitk", splits) when the 256 x 256 tiles
-    leave CUs idle, else ("slab", 1)."""
-    if 0 < M <= SMALL_MAX_TOKENS:
-        return "small", mx_linear_small_choose(M, K, N)
-    sp = mx_linear_splitk_choose(M, K, N)
-    return ("splitk", sp) if sp > 1 else ("slab", 1)
+    """The default kernel plan of an M x K x N slab linear
+    (mx_linear_plan_default): ("small", splits), ("splitk", splits) or
+    ("slab", 1)."""
+    return _plan_out(lib().mx_linear_plan_default, M, K, N)
 
 
-def plan_ws_bytes(plan, M, N):
-    """Workspace bytes of a plan from plan_linear (0 when none is needed)."""
+def plan_lookup(M, K, N, gelu=False):
+    """The tuned plan of this shape if mx_linear_tune cached one, else the
+    default plan (mx_linear_plan_lookup)."""
+    return _plan_out(lib().mx_linear_plan_lookup, M, K, N, MX_EPI_GELU_TANH if gelu else MX_EPI_NONE)
+
+
+def plan_ws_bytes(plan, M, N, K=64):
+    """Workspace bytes of a plan (mx_linear_plan_ws_bytes; K matters only to
+    "balanced")."""
     kind, sp = plan
-    if kind == "small":
-        return mx_linear_small_ws_bytes(M, N, sp)
-    if kind == "splitk":
-        return mx_linear_splitk_ws_bytes(M, N, sp)
-    return 0
+    return lib().mx_linear_plan_ws_bytes(PLAN_KINDS[kind], sp, M, K, N)
+
+
+def mx_linear_tune_ws_bytes(M, K, N):
+    return lib().mx_linear_tune_ws_bytes(M, K, N)
+
+
+def mx_linear_plan_clear():
+    lib().mx_linear_plan_clear()
+
+
+def _plan_call(x, w, bias, y):
+    dev, M, N, K = _slab_linear_args(x, w, bias)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    return dev, M, N, K, y
+
+
+def _ws_args(workspace, dev):
+    if workspace is None:
+        return None, 0
+    _need(workspace, "workspace", torch.uint8, dev)
+    return workspace, workspace.numel()
 
 
 def mx_linear_slab_planned(plan, x, w, bias=None, gelu=False, y=None, workspace=None):
-    """mx_linear_slab through the kernel a plan_linear plan names."""
+    """mx_linear_slab through the kernel a plan names (mx_linear_slab_plan);
+    workspace: uint8 of at least plan_ws_bytes(plan, M, N, K) bytes
+    (allocated here when None and needed)."""
+    dev, M, N, K, y = _plan_call(x, w, bias, y)
     kind, sp = plan
-    if kind == "small":
-        return mx_linear_slab_small(x, w, bias, gelu=gelu, y=y, splits=sp, workspace=workspace)
-    if kind == "splitk":
-        return mx_linear_slab_splitk(x, w, bias, gelu=gelu, y=y, splits=sp, workspace=workspace)
-    return mx_linear_slab(x, w, bias, gelu=gelu, y=y)
+    need = lib().mx_linear_plan_ws_bytes(PLAN_KINDS[kind], sp, M, K, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    workspace, nb = _ws_args(workspace, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(lib().mx_linear_slab_plan(PLAN_KINDS[kind], sp, _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N,
+                                         _ptr(bias), epi, _ptr(y), _ptr(workspace), nb, _stream(dev)))
+    return y
+
+
+def mx_linear_tune(x, w, bias=None, gelu=False, y=None, workspace=None, reps=10):
+    """Times the candidate plans of this shape on these operands, caches the
+    fastest (mx_linear_tune) and returns it as (kind, splits). workspace:
+    uint8 of at least mx_linear_tune_ws_bytes(M, K, N) bytes (allocated here
+    when None). Synchronizes the current stream."""
+    dev, M, N, K, y = _plan_call(x, w, bias, y)
+    if workspace is None:
+        workspace = torch.empty((max(mx_linear_tune_ws_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
+    workspace, nb = _ws_args(workspace, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        return _plan_out(lib().mx_linear_tune, _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi,
+                         _ptr(y), _ptr(workspace), nb, int(reps), _stream(dev))
+
+
+def mx_linear_slab_auto(x, w, bias=None, gelu=False, y=None, workspace=None):
+    """mx_linear_slab through the cached (tuned) or default plan of this shape
+    (mx_linear_slab_auto); workspace: uint8 of at least the plan's workspace
+    (mx_linear_tune_ws_bytes always suffices; allocated here when None and
+    needed)."""
+    dev, M, N, K, y = _plan_call(x, w, bias, y)
+    if workspace is None:
+        with torch.cuda.device(dev):
+            kind, sp = plan_lookup(M, K, N, gelu)
+        need = lib().mx_linear_plan_ws_bytes(PLAN_KINDS[kind], sp, M, K, N)
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    workspace, nb = _ws_args(workspace, dev)
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(lib().mx_linear_slab_auto(_ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi,
+                                         _ptr(y), _ptr(workspace), nb, _stream(dev)))
+    return y
 
 
 def mx_linear_balanced_ws_bytes(M, K, N):

@@ -10,6 +10,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "mx.h"
 #include "mx_internal.h"
@@ -46,6 +49,11 @@ constexpr int64_t kMaxRows = int64_t(1) << 30;
 constexpr int64_t kSplitTargetWorkgroups = 256;  // one workgroup per CU of an MI355X
 constexpr int64_t kMaxSplitWorkgroups = int64_t(1) << 24;
 constexpr int64_t kMaxAutoSplits = 8;  // 128 x 5120 x 5120: 8 splits 19.5 us, 12 splits 20.7 us
+// Default plan: the few-token kernel up to 256 tokens (MI355X, K = 5120: 16.0
+// vs 20.4 us at 128 tokens, 19.1 vs 25.7 at 256; split-K wins from 512).
+constexpr int64_t kSmallMaxTokens = 256;
+constexpr int64_t kTuneSmallMaxTokens = 1024;  // the tuner tries the few-token kernel up to here
+constexpr int kMaxTuneCandidates = 24;
 
 int check_k(int64_t K) {
   if (K <= 0 || K % 32 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "K = %lld must be a positive multiple of 32", (long long)K);
@@ -549,6 +557,213 @@ int mx_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int
   return finish(mx::launch_linear_slab_balanced(xq, xs, M, K, wq, ws, N, bias, epilogue, y, ncu, (float*)workspace,
                                                 (hipStream_t)stream),
                 "linear launch");
+}
+
+/* ---- Per-shape plans: default rule, tuner, process-local cache ---------- */
+
+int mx_linear_plan_default(int64_t M, int64_t K, int64_t N, int* kind, int* splits) {
+  if (kind == nullptr || splits == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL kind or splits");
+  if (M < 0 || N < 0 || K < 64 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN)
+    return fail(MX_ERR_INVALID_ARGUMENT, "bad shape %lld x %lld x %lld", (long long)M, (long long)K, (long long)N);
+  if (M > 0 && M <= kSmallMaxTokens) {
+    *kind = MX_PLAN_SMALL;
+    *splits = mx_linear_small_choose(M, K, N);
+  } else {
+    const int s = mx_linear_splitk_choose(M, K, N);
+    *kind = s > 1 ? MX_PLAN_SPLITK : MX_PLAN_SLAB;
+    *splits = s > 1 ? s : 1;
+  }
+  t_msg[0] = '\0';
+  return MX_OK;
+}
+
+int64_t mx_linear_plan_ws_bytes(int kind, int splits, int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 0 || K < 64 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN) return -1;
+  switch (kind) {
+    case MX_PLAN_SLAB:
+      return splits == 1 ? 0 : -1;
+    case MX_PLAN_SPLITK:
+      return mx_linear_splitk_ws_bytes(M, N, splits);
+    case MX_PLAN_SMALL:
+      return mx_linear_small_ws_bytes(M, N, splits);
+    case MX_PLAN_BALANCED:
+      return splits == 1 ? mx_linear_balanced_ws_bytes(M, K, N) : -1;
+    default:
+      return -1;
+  }
+}
+
+int mx_linear_slab_plan(int kind, int splits, const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                        const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y,
+                        void* workspace, int64_t workspace_bytes, void* stream) {
+  switch (kind) {
+    case MX_PLAN_SLAB:
+      if (splits != 1) return fail(MX_ERR_INVALID_ARGUMENT, "the slab plan takes splits = 1, not %d", splits);
+      return mx_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, stream);
+    case MX_PLAN_SPLITK:
+      return mx_linear_slab_splitk(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, workspace, workspace_bytes,
+                                   stream);
+    case MX_PLAN_SMALL:
+      return mx_linear_slab_small(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, workspace, workspace_bytes,
+                                  stream);
+    case MX_PLAN_BALANCED:
+      if (splits != 1) return fail(MX_ERR_INVALID_ARGUMENT, "the balanced plan takes splits = 1, not %d", splits);
+      return mx_linear_slab_balanced(xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace, workspace_bytes, stream);
+    default:
+      return fail(MX_ERR_INVALID_ARGUMENT, "unknown plan kind %d", kind);
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+struct Plan {
+  int kind, splits;
+};
+
+// Candidate plans of the tuner for one shape (the default plan first).
+int tune_candidates(int64_t M, int64_t K, int64_t N, Plan* out, int cap) {
+  int n = 0;
+  auto add = [&](int kind, int splits) {
+    for (int i = 0; i < n; ++i)
+      if (out[i].kind == kind && out[i].splits == splits) return;
+    if (n < cap) out[n++] = Plan{kind, splits};
+  };
+  int k0, s0;
+  if (mx_linear_plan_default(M, K, N, &k0, &s0) != MX_OK) return 0;
+  add(k0, s0);
+  add(MX_PLAN_SLAB, 1);
+  const int64_t nh = K / 64;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  static const int kSplits[] = {2, 3, 4, 6, 8};
+  if (tiles < cu_count())
+    for (int s : kSplits)
+      if (s <= nh) add(MX_PLAN_SPLITK, s);
+  if (M <= kTuneSmallMaxTokens) {
+    add(MX_PLAN_SMALL, 1);
+    for (int s : kSplits)
+      if (s <= nh) add(MX_PLAN_SMALL, s);
+  }
+  if (tiles > cu_count() && tiles % cu_count() != 0 && mx_linear_balanced_ws_bytes(M, K, N) > 0)
+    add(MX_PLAN_BALANCED, 1);
+  return n;
+}
+
+using PlanKey = std::tuple<int, int64_t, int64_t, int64_t, int>;  // device, M, K, N, epilogue
+std::mutex g_plan_mutex;
+std::map<PlanKey, Plan> g_plans;
+
+bool cached_plan(const PlanKey& key, Plan* p) {
+  std::lock_guard<std::mutex> lock(g_plan_mutex);
+  auto it = g_plans.find(key);
+  if (it == g_plans.end()) return false;
+  *p = it->second;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mx_linear_tune_ws_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 0 || K < 64 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN) return -1;
+  Plan c[kMaxTuneCandidates];
+  const int n = tune_candidates(M, K, N, c, kMaxTuneCandidates);
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) need = std::max(need, mx_linear_plan_ws_bytes(c[i].kind, c[i].splits, M, K, N));
+  return need;
+}
+
+int mx_linear_tune(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws,
+                   int64_t N, const void* bias, int epilogue, void* y, void* workspace, int64_t workspace_bytes,
+                   int reps, void* stream, int* kind, int* splits) {
+  if (kind == nullptr || splits == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL kind or splits");
+  if (reps < 1 || reps > 1000) return fail(MX_ERR_INVALID_ARGUMENT, "reps = %d must be in [1, 1000]", reps);
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK) return st;
+  if (M == 0 || N == 0) return fail(MX_ERR_INVALID_ARGUMENT, "nothing to tune for an empty shape");
+  if ((st = check_device()) != MX_OK) return st;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  Plan c[kMaxTuneCandidates];
+  const int n = tune_candidates(M, K, N, c, kMaxTuneCandidates);
+  hipEvent_t ev[2];
+  if ((e = hipEventCreate(&ev[0])) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if ((e = hipEventCreate(&ev[1])) != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return hip_fail(e, "hipEventCreate");
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  Plan best{-1, 0};
+  float best_ms = 0.f;
+  int result = MX_OK;
+  for (int i = 0; i < n && result == MX_OK; ++i) {
+    const int64_t need = mx_linear_plan_ws_bytes(c[i].kind, c[i].splits, M, K, N);
+    if (need < 0 || need > workspace_bytes) continue;  // the caller's workspace does not fit this candidate
+    // Warm-up run: a candidate the entry point rejects (a size limit) is skipped.
+    if (mx_linear_slab_plan(c[i].kind, c[i].splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace,
+                            workspace_bytes, stream) != MX_OK)
+      continue;
+    float ms = 0.f;
+    if ((e = hipEventRecord(ev[0], hs)) != hipSuccess) { result = hip_fail(e, "hipEventRecord"); break; }
+    for (int r = 0; r < reps && result == MX_OK; ++r)
+      result = mx_linear_slab_plan(c[i].kind, c[i].splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace,
+                                   workspace_bytes, stream);
+    if (result != MX_OK) break;
+    if ((e = hipEventRecord(ev[1], hs)) != hipSuccess) { result = hip_fail(e, "hipEventRecord"); break; }
+    if ((e = hipEventSynchronize(ev[1])) != hipSuccess) { result = hip_fail(e, "hipEventSynchronize"); break; }
+    if ((e = hipEventElapsedTime(&ms, ev[0], ev[1])) != hipSuccess) { result = hip_fail(e, "hipEventElapsedTime"); break; }
+    if (best.kind < 0 || ms < best_ms) {
+      best = c[i];
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  if (result != MX_OK) return result;
+  if (best.kind < 0) return fail(MX_ERR_INVALID_ARGUMENT, "no candidate plan fits a workspace of %lld bytes",
+                                 (long long)workspace_bytes);
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mutex);
+    g_plans[PlanKey{dev, M, K, N, epilogue}] = best;
+  }
+  *kind = best.kind;
+  *splits = best.splits;
+  t_msg[0] = '\0';
+  return MX_OK;
+}
+
+int mx_linear_plan_lookup(int64_t M, int64_t K, int64_t N, int epilogue, int* kind, int* splits) {
+  if (kind == nullptr || splits == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL kind or splits");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  Plan p;
+  if (cached_plan(PlanKey{dev, M, K, N, epilogue}, &p)) {
+    *kind = p.kind;
+    *splits = p.splits;
+    t_msg[0] = '\0';
+    return MX_OK;
+  }
+  return mx_linear_plan_default(M, K, N, kind, splits);
+}
+
+int mx_linear_slab_auto(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                        const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  int kind, splits;
+  int st = check_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if ((st = mx_linear_plan_lookup(M, K, N, epilogue, &kind, &splits)) != MX_OK) return st;
+  return mx_linear_slab_plan(kind, splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace, workspace_bytes,
+                             stream);
+}
+
+void mx_linear_plan_clear(void) {
+  std::lock_guard<std::mutex> lock(g_plan_mutex);
+  g_plans.clear();
 }
 
 }  // extern "C"

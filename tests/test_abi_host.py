@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 8
+    assert L.mx_abi_version() == 9
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -328,3 +328,46 @@ def test_per_shape_plan():
     assert pkg.plan_ws_bytes(("small", 1), 128, 5120) == 0
     assert pkg.plan_ws_bytes(("splitk", 3), 512, 10240) == 3 * 2 * 40 * 65536 * 4
     assert pkg.plan_ws_bytes(("slab", 1), 75348, 15360) == 0
+    assert pkg.plan_ws_bytes(("balanced", 1), 75348, 5120, 5120) == 8 * 12 * 65536 * 4
+
+
+def test_plan_entry_points_host_side(L):
+    import ctypes
+
+    kind, splits = ctypes.c_int(-1), ctypes.c_int(-1)
+
+    def default(M, K, N):
+        st = L.mx_linear_plan_default(M, K, N, ctypes.byref(kind), ctypes.byref(splits))
+        return st, kind.value, splits.value
+
+    # The rule: few-token kernel up to 256 tokens, split-K while the 256 x 256
+    # tiles are fewer than the CUs (256 assumed without a GPU), else slab.
+    assert default(128, 5120, 5120) == (0, 2, 3)
+    assert default(256, 5120, 5120) == (0, 2, 1)
+    assert default(512, 5120, 10240) == (0, 1, 3)
+    assert default(75348, 5120, 15360) == (0, 0, 1)
+    assert default(0, 64, 64) == (0, 0, 1)  # empty: nothing to split
+    assert default(8, 96, 64)[0] == 1 and default(-1, 64, 64)[0] == 1
+    assert L.mx_linear_plan_default(8, 64, 64, None, ctypes.byref(splits)) == 1
+    # Workspace of each kind
+    assert L.mx_linear_plan_ws_bytes(0, 1, 75348, 5120, 15360) == 0
+    assert L.mx_linear_plan_ws_bytes(0, 2, 75348, 5120, 15360) == -1  # slab takes splits 1
+    assert L.mx_linear_plan_ws_bytes(1, 3, 512, 5120, 10240) == L.mx_linear_splitk_ws_bytes(512, 10240, 3)
+    assert L.mx_linear_plan_ws_bytes(2, 3, 128, 5120, 5120) == 3 * 128 * 5120 * 4
+    assert L.mx_linear_plan_ws_bytes(3, 1, 75348, 5120, 5120) == L.mx_linear_balanced_ws_bytes(75348, 5120, 5120)
+    assert L.mx_linear_plan_ws_bytes(7, 1, 8, 64, 64) == -1
+    # The tuner's workspace covers its largest candidate: at 128 x 5120 x 5120
+    # split-K with 8 ranges (8 x 20 partial tiles of 256 KiB).
+    assert L.mx_linear_tune_ws_bytes(128, 5120, 5120) == 8 * 20 * 65536 * 4
+    assert L.mx_linear_tune_ws_bytes(8, 96, 64) == -1
+    # Argument errors before any device call
+    E = 0x50000000
+    assert L.mx_linear_slab_plan(9, 1, P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20,
+                                 P(0)) == 1
+    assert L.mx_linear_slab_plan(0, 2, P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20,
+                                 P(0)) == 1
+    assert L.mx_linear_tune(P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20, 0, P(0),
+                            ctypes.byref(kind), ctypes.byref(splits)) == 1  # reps 0
+    assert L.mx_linear_tune(P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20, 5, P(0),
+                            None, ctypes.byref(splits)) == 1
+    L.mx_linear_plan_clear()

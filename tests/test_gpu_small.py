@@ -112,3 +112,38 @@ def test_planned_linear_matches_oracle(M, K, N, kind):
     torch.cuda.synchronize()
     yref, S = oracle_linear(x, w, b, True)
     assert_linear_close(y, yref, S, "gelu_tanh", what=f"planned {kind}")
+
+
+@pytest.mark.parametrize("M,K,N,gelu", [(128, 5120, 5120, False), (512, 1024, 1024, True), (300, 640, 2048, False)])
+def test_tuned_plan_is_cached_and_matches_oracle(M, K, N, gelu):
+    # Warm-up tuning picks one of the candidate kernels for the shape, caches
+    # it, and the auto entry point then runs that plan: same bits as calling
+    # the plan directly, and the oracle's result within the tolerance.
+    print(f"tune M={M} K={K} N={N}", flush=True)
+    mx().mx_linear_plan_clear()
+    assert mx().plan_lookup(M, K, N, gelu) == mx().plan_linear(M, K, N)
+    x, w, b, xs, ws, bd = operands(M, K, N, seed=M + K + 7)
+    plan = mx().mx_linear_tune(xs, ws, bd, gelu=gelu, reps=3)
+    assert plan[0] in ("slab", "splitk", "small", "balanced")
+    assert mx().plan_lookup(M, K, N, gelu) == plan
+    y_auto = mx().mx_linear_slab_auto(xs, ws, bd, gelu=gelu)
+    y_plan = mx().mx_linear_slab_planned(plan, xs, ws, bd, gelu=gelu)
+    torch.cuda.synchronize()
+    assert torch.equal(y_auto.view(torch.int16), y_plan.view(torch.int16))
+    yref, S = oracle_linear(x, w, b, gelu)
+    assert_linear_close(y_auto, yref, S, "gelu_tanh" if gelu else "none", what=f"auto {plan}")
+    mx().mx_linear_plan_clear()
+    assert mx().plan_lookup(M, K, N, gelu) == mx().plan_linear(M, K, N)
+
+
+def test_tune_without_workspace_keeps_to_plans_that_need_none():
+    M, K, N = 128, 1024, 1024
+    x, w, b, xs, ws, bd = operands(M, K, N, seed=5)
+    empty = torch.empty((0,), dtype=torch.uint8, device=dev())
+    plan = mx().mx_linear_tune(xs, ws, bd, workspace=empty, reps=2)
+    assert plan in (("slab", 1), ("small", 1))
+    y = mx().mx_linear_slab_auto(xs, ws, bd)
+    torch.cuda.synchronize()
+    yref, S = oracle_linear(x, w, b, False)
+    assert_linear_close(y, yref, S, what=f"auto {plan}")
+    mx().mx_linear_plan_clear()
