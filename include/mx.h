@@ -287,7 +287,8 @@ int64_t mx_linear_tune_ws_bytes(int64_t M, int64_t K, int64_t N);
 
 /* Warm-up tuning of one shape on the caller's operands: runs each candidate
  * plan once, then `reps` times between two HIP events on `stream` (1 <=
- * reps <= 1000), and keeps the fastest. Candidates: the default plan; the
+ * reps <= 1000), queued behind a short delay kernel so that they run back to
+ * back (GPU time, as under graph replay), and keeps the fastest. Candidates: the default plan; the
  * slab GEMM; split-K with 2, 3, 4, 6, 8 ranges when the 256 x 256 tiles are
  * fewer than the device's CUs; the few-token kernel with 1, 2, 3, 4, 6, 8
  * ranges for M <= 1024; the balanced GEMM when the tiles leave a partial

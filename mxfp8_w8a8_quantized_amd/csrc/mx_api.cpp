@@ -706,7 +706,11 @@ int mx_linear_tune(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, c
     if (mx_linear_slab_plan(c[i].kind, c[i].splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace,
                             workspace_bytes, stream) != MX_OK)
       continue;
+    // The timed runs queue behind a delay long enough for the host to submit
+    // them all (about 10 us per launch, at most two launches per run), so the
+    // events measure the GPU's back-to-back time, not the host's launch rate.
     float ms = 0.f;
+    if ((e = mx::launch_delay(std::min(20 * reps + 50, 20000), hs)) != hipSuccess) { result = hip_fail(e, "delay launch"); break; }
     if ((e = hipEventRecord(ev[0], hs)) != hipSuccess) { result = hip_fail(e, "hipEventRecord"); break; }
     for (int r = 0; r < reps && result == MX_OK; ++r)
       result = mx_linear_slab_plan(c[i].kind, c[i].splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace,

@@ -58,6 +58,10 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
 // into `part` and reduces them in range order. small_tiles gives the tile
 // count. 1 <= splits <= K/64, N % 16 == 0.
 int64_t small_tiles(int64_t M, int64_t N);
+
+// A one-wave kernel that occupies `stream` for about `microseconds` (the
+// tuner queues its timed runs behind it, so that they run back to back).
+hipError_t launch_delay(int microseconds, hipStream_t stream);
 hipError_t launch_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
                                     const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
                                     float* part, hipStream_t stream);

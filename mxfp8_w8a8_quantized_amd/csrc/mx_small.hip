@@ -300,7 +300,24 @@ hipError_t launch_small_kernel(const SmallParams& p, int nwg, hipStream_t st) {
   return hipGetLastError();
 }
 
+// One wave that waits until `ticks` of the constant-rate wall clock have
+// passed (bounded: it always exits).
+__global__ __launch_bounds__(64) void delay_kernel(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
 }  // namespace
+
+hipError_t launch_delay(int microseconds, hipStream_t stream) {
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+  const uint64_t ticks = (uint64_t)(khz > 0 ? khz : 100000) * (uint64_t)microseconds / 1000u;
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, stream, ticks);
+  return hipGetLastError();
+}
 
 int64_t small_tiles(int64_t M, int64_t N) { return ((M + TM - 1) / TM) * ((N + TN - 1) / TN); }
 
