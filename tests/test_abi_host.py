@@ -241,6 +241,10 @@ def test_small_rejects_bad_arguments(L):
     assert call(epi=7) == 1
     assert call(N=264) == 2
     assert call(M=0) == 0 and call(N=0) == 0
+    # 32-bit K-range offsets: (K/64 + 16) * 64 * rows must stay below 2^31
+    # (checked before the buffers' extents, so fake addresses do).
+    assert call(M=1 << 20, K=5120, nb=1 << 40) == 2  # (80 + 16) * 64 * 2^20 > 2^31
+    assert call(M=8, K=5120, N=1 << 20, nb=1 << 40) == 2
 
 
 def test_balanced_plan_sizes(L):
