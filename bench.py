@@ -157,6 +157,29 @@ def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
     }
 
 
+def workload_roofline(layers, flop, ms):
+    """Where a workload stands against its bound, per step at time ms:
+    algorithmic HBM bytes (bf16 activations read, E4M3 + E8M0 codes written
+    and read back by the GEMM, weight codes + scales, f16 bias, bf16 output)
+    against 8 TB/s, and 2*M*N*K against the 5.0 PFLOP/s dense MXFP8 peak. The
+    bound is the one with the larger time at peak (HBM for the 128-token
+    linear, MFMA for the others)."""
+    nbytes = 0
+    for shp, _, _ in layers:
+        act = shp.M * shp.K
+        nbytes += act * 2 + 2 * (act + act // 32)  # bf16 in; codes + scales written, then read
+        nbytes += shp.N * shp.K + shp.N * shp.K // 32 + shp.N * 2 + shp.M * shp.N * 2
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    t_mfma = flop / (PEAK_MXFP8_TFLOPS * 1e12)
+    if t_hbm > t_mfma:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "bytes": nbytes}
+    ach = flop / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_MXFP8_TFLOPS, 4), "bytes": nbytes}
+
+
 def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
     """The other Wan2.2-A14B linears on the slab path, one step each: every
     linear quantizes its activation into a slab and runs the GEMM; the FFN's
@@ -221,6 +244,7 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
             "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
             "graph_ms": round(g_ms, 4),
             "graph_TFLOPs": round(flop / (g_ms * 1e-3) / 1e12, 2),
+            "roofline": workload_roofline(layers, flop, g_ms),
         }
         if [shp.name for shp, _, _ in layers] == ["ffn.net.0.proj", "ffn.net.2"]:
             # The same pair with the requantization fused into the up-projection.
