@@ -702,10 +702,15 @@ int mx_linear_tune(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, c
   for (int i = 0; i < n && result == MX_OK; ++i) {
     const int64_t need = mx_linear_plan_ws_bytes(c[i].kind, c[i].splits, M, K, N);
     if (need < 0 || need > workspace_bytes) continue;  // the caller's workspace does not fit this candidate
-    // Warm-up run: a candidate the entry point rejects (a size limit) is skipped.
-    if (mx_linear_slab_plan(c[i].kind, c[i].splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace,
-                            workspace_bytes, stream) != MX_OK)
-      continue;
+    // Warm-up run: a candidate the entry point rejects (a size limit) is
+    // skipped; a HIP failure ends the tuning.
+    const int wst = mx_linear_slab_plan(c[i].kind, c[i].splits, xq, xs, M, K, wq, ws, N, bias, epilogue, y, workspace,
+                                        workspace_bytes, stream);
+    if (wst == MX_ERR_HIP) {
+      result = wst;
+      break;
+    }
+    if (wst != MX_OK) continue;
     // The timed runs queue behind a delay long enough for the host to submit
     // them all (about 10 us per launch, at most two launches per run), so the
     // events measure the GPU's back-to-back time, not the host's launch rate.
