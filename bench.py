@@ -18,7 +18,10 @@ Prints ONE JSON line. Besides the contract fields it carries
                 peak, from its per-launch HIP-event times on the launch
                 stream; `traffic` is the HBM bytes per launch from the
                 committed rocprofv3 counter summary when that was taken on
-                the current kernel sources, else null;
+                the current kernel sources, else null; `mfma_probe_TFLOPs`
+                is the scaled MFMA's sustained rate from registers (no
+                memory traffic) on this workload's codes and on zeros, and
+                `frac_of_probe` the GEMM against the former;
   cpu_baseline  the float64 CPU oracle timed on a bounded row sample of the
                 same inputs;
   extra         the activation quantizer's bandwidth, the same step on
@@ -157,6 +160,32 @@ def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
         "sample": f"first {rows} of {M} token rows x all {N} outputs (K={K}): float64 activation quantization + "
         f"dequantized GEMM with its sum|a||b| bound, {dt:.1f} s; FLOP counted as 2*rows*N*K",
     }
+
+
+def mfma_probe(torch, mx, dev, a_codes, b_codes, iters=2000, reps=10):
+    """The scaled FP8 MFMA's sustained rate with operands in registers and no
+    memory traffic (mx_probe_mfma, one 4-wave workgroup per CU), on this
+    workload's own activation and weight codes and on zero codes: the clock
+    the chip holds depends on the operand bits, so this is the ceiling the
+    GEMM's MFMAs face, next to the 5.0 PFLOP/s nominal peak."""
+    n = 8 << 20  # bytes of codes each lane group draws from
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty((ncu * 256,), dtype=torch.float32, device=dev)
+    out = {}
+    for name, a, b in (("workload_codes", a_codes.view(-1)[:n], b_codes.view(-1)[:n]),
+                       ("zero_codes", torch.zeros(n, dtype=torch.uint8, device=dev),
+                        torch.zeros(n, dtype=torch.uint8, device=dev))):
+        for _ in range(5):
+            flop = mx.mx_probe_mfma(a, b, iters, ncu, sink)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            mx.mx_probe_mfma(a, b, iters, ncu, sink)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[name] = round(flop * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12, 1)
+    out["unit"] = "TFLOP/s"
+    return out
 
 
 def workload_roofline(layers, flop, ms):
@@ -408,6 +437,8 @@ def main():
     gemm_ms = mean(g_ms)
     achieved = flop / (gemm_ms * 1e-3) / 1e12
 
+    probe = mfma_probe(torch, mx, dev, xsl.q, wsl.q)
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -445,6 +476,8 @@ def main():
             "traffic": traffic,
             "kernel": "linear_slab_kernel (block-scaled GEMM)",
             "launch_ms": round(gemm_ms, 4),
+            "mfma_probe_TFLOPs": probe,
+            "frac_of_probe": round(achieved / probe["workload_codes"], 4),
             "kernel_source_hash": kernel_source_hash(),
         },
     }

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 9
+#define MX_ABI_VERSION 10
 
 typedef enum {
   MX_OK = 0,
@@ -318,6 +318,26 @@ int mx_linear_slab_auto(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t
 
 /* Empties the plan cache. */
 void mx_linear_plan_clear(void);
+
+/* ------------------------------------------------------------------------
+ * Measurement. The MFMA peak that the 5.0 PFLOP/s figure assumes needs the
+ * full clock, which the chip does not hold when the matrix cores work on
+ * real operand bits. This probe measures what the scaled FP8 MFMA sustains
+ * with no memory traffic at all, on codes the caller chooses (for instance
+ * the workload's own codes, or zeros).
+ * ------------------------------------------------------------------------ */
+
+/* Launches `blocks` workgroups of 4 waves (one per CU gives the whole GPU):
+ * each lane reads 128 bytes of A codes and 128 bytes of B codes (32-bit words
+ * taken modulo bytes / 4 from a and b, any E4M3 bytes), then issues 16 * iters
+ * independent v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) from
+ * registers and writes one float per thread to sink (blocks * 256 floats).
+ * Work: blocks * 4 * 16 * iters * 2 * 32 * 32 * 64 FLOP; time it with events
+ * on `stream`. a, b, sink: device pointers, 4-byte aligned; 4 <= bytes <=
+ * 2^31, a multiple of 4; 1 <= iters <= 2^20; 1 <= blocks <= 65536 (else
+ * MX_ERR_INVALID_ARGUMENT). */
+int mx_probe_mfma(const uint8_t* a, const uint8_t* b, int64_t bytes, int iters, int blocks,
+                  float* sink, void* stream);
 
 /* Workspace bytes mx_linear_slab_balanced needs on the current device: the
  * fp32 partial tiles of its split last round, 0 when it splits nothing; -1 on

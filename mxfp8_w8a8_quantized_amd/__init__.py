@@ -68,6 +68,7 @@ SIGNATURES = {
     "mx_linear_plan_lookup": ([_I64, _I64, _I64, _INT, _PI, _PI], _INT),
     "mx_linear_slab_auto": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "mx_linear_plan_clear": ([], None),
+    "mx_probe_mfma": ([_P, _P, _I64, _INT, _INT, _P, _P], _INT),
     "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
@@ -568,6 +569,22 @@ def mx_linear_slab_auto(x, w, bias=None, gelu=False, y=None, workspace=None):
         _check(lib().mx_linear_slab_auto(_ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi,
                                          _ptr(y), _ptr(workspace), nb, _stream(dev)))
     return y
+
+
+def mx_probe_mfma(a, b, iters, blocks, sink):
+    """Launches the MFMA throughput probe (mx_probe_mfma) on uint8 code
+    tensors a, b (same byte count, a multiple of 4) with a float32 sink of at
+    least blocks * 256 elements; returns the FLOP it performs. Time it with
+    events on the current stream."""
+    dev = a.device
+    _need(a, "a", torch.uint8, dev)
+    _need(b, "b", torch.uint8, dev)
+    _need(sink, "sink", torch.float32, dev)
+    if a.numel() != b.numel() or sink.numel() < blocks * 256:
+        raise ValueError("a and b must have equal sizes and sink at least blocks * 256 floats")
+    with torch.cuda.device(dev):
+        _check(lib().mx_probe_mfma(_ptr(a), _ptr(b), a.numel(), int(iters), int(blocks), _ptr(sink), _stream(dev)))
+    return float(blocks) * 4 * 16 * iters * 2 * 32 * 32 * 64
 
 
 def mx_linear_balanced_ws_bytes(M, K, N):

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libmxfp8.so")
-SOURCES = ["mx_api.cpp", "mx_quant.hip", "mx_pc.hip", "mx_gemm.hip", "mx_small.hip"]
+SOURCES = ["mx_api.cpp", "mx_quant.hip", "mx_pc.hip", "mx_gemm.hip", "mx_small.hip", "mx_probe.hip"]
 
 # Device code is built without packed-FP32 instructions (v_pk_*_f32).
 HIP_FLAGS = [

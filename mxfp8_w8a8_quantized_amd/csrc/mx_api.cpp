@@ -770,6 +770,21 @@ int mx_linear_slab_auto(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t
                              stream);
 }
 
+int mx_probe_mfma(const uint8_t* a, const uint8_t* b, int64_t bytes, int iters, int blocks, float* sink,
+                  void* stream) {
+  if (a == nullptr || b == nullptr || sink == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(sink, 4))
+    return fail(MX_ERR_INVALID_ARGUMENT, "a, b and sink must be 4-byte aligned");
+  if (bytes < 4 || bytes % 4 != 0 || bytes > (int64_t(1) << 31))
+    return fail(MX_ERR_INVALID_ARGUMENT, "bytes = %lld must be a positive multiple of 4, at most 2^31", (long long)bytes);
+  if (iters < 1 || iters > (1 << 20)) return fail(MX_ERR_INVALID_ARGUMENT, "iters = %d must be in [1, 2^20]", iters);
+  if (blocks < 1 || blocks > 65536) return fail(MX_ERR_INVALID_ARGUMENT, "blocks = %d must be in [1, 65536]", blocks);
+  int st;
+  if ((st = check_device()) != MX_OK) return st;
+  (void)hipGetLastError();
+  return finish(mx::launch_mfma_probe(a, b, bytes, iters, blocks, sink, (hipStream_t)stream), "probe launch");
+}
+
 void mx_linear_plan_clear(void) {
   std::lock_guard<std::mutex> lock(g_plan_mutex);
   g_plans.clear();

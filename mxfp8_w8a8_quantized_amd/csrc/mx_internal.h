@@ -59,6 +59,12 @@ hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64
 // count. 1 <= splits <= K/64, N % 16 == 0.
 int64_t small_tiles(int64_t M, int64_t N);
 
+// Measurement probe (mx_probe.hip): `blocks` workgroups of 4 waves, each
+// lane loading 128 bytes of A and B codes (word index modulo bytes / 4), then
+// 16 * iters scaled 32x32x64 MFMAs; one float per thread to sink.
+hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, int64_t bytes, int iters, int blocks, float* sink,
+                             hipStream_t stream);
+
 // A one-wave kernel that occupies `stream` for about `microseconds` (the
 // tuner queues its timed runs behind it, so that they run back to back).
 hipError_t launch_delay(int microseconds, hipStream_t stream);

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 9
+    assert L.mx_abi_version() == 10
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -375,3 +375,14 @@ def test_plan_entry_points_host_side(L):
     assert L.mx_linear_tune(P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20, 5, P(0),
                             None, ctypes.byref(splits)) == 1
     L.mx_linear_plan_clear()
+
+
+def test_probe_rejects_bad_arguments(L):
+    f = L.mx_probe_mfma
+    assert f(P(0), P(B), 1024, 10, 256, P(D), P(0)) == 1
+    assert f(P(A), P(B), 1022, 10, 256, P(D), P(0)) == 1  # bytes % 4
+    assert f(P(A), P(B), 0, 10, 256, P(D), P(0)) == 1
+    assert f(P(A), P(B), (1 << 31) + 4, 10, 256, P(D), P(0)) == 1
+    assert f(P(A), P(B), 1024, 0, 256, P(D), P(0)) == 1
+    assert f(P(A), P(B), 1024, 10, 0, P(D), P(0)) == 1
+    assert f(P(A + 2), P(B), 1024, 10, 256, P(D), P(0)) == 1

@@ -147,3 +147,20 @@ def test_tune_without_workspace_keeps_to_plans_that_need_none():
     yref, S = oracle_linear(x, w, b, False)
     assert_linear_close(y, yref, S, what=f"auto {plan}")
     mx().mx_linear_plan_clear()
+
+
+def test_mfma_probe_sums_exactly():
+    # Codes 0x38 (1.0) everywhere with unit block scales: each MFMA adds 64 to
+    # each of its 32 x 32 accumulators, so a thread's sum of its 16 blocks of
+    # 16 accumulators after `iters` rounds is 256 * 64 * iters, exact in fp32.
+    d = dev()
+    ones = torch.full((4096,), 0x38, dtype=torch.uint8, device=d)
+    sink = torch.full((2 * 256,), float("nan"), dtype=torch.float32, device=d)
+    flop = mx().mx_probe_mfma(ones, ones, 3, 2, sink)
+    torch.cuda.synchronize()
+    assert flop == 2 * 4 * 16 * 3 * 2 * 32 * 32 * 64
+    assert torch.equal(sink.cpu(), torch.full((512,), 256.0 * 64 * 3))
+    zeros = torch.zeros(4096, dtype=torch.uint8, device=d)
+    mx().mx_probe_mfma(zeros, ones, 3, 2, sink)
+    torch.cuda.synchronize()
+    assert not sink.any()
