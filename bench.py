@@ -24,7 +24,9 @@ Prints ONE JSON line. Besides the contract fields it carries
                 `frac_of_probe` the GEMM against the former;
   cpu_baseline  the float64 CPU oracle timed on a bounded row sample of the
                 same inputs;
-  extra         the activation quantizer's bandwidth, the same step on
+  extra         p10/p50/p90 of the step and GEMM times, the step with cold
+                caches (a 1 GiB write before each rep), the activation
+                quantizer's bandwidth, the same step on
                 row-major operands (mx_quantize_act + mx_linear_q), the
                 fused-prologue path (mx_linear), the weight quantizer, the
                 other Wan2.2 linears, and one whole denoise step's 400
@@ -160,6 +162,37 @@ def cpu_baseline(x_cpu, w_cpu, b_cpu, rows):
         "sample": f"first {rows} of {M} token rows x all {N} outputs (K={K}): float64 activation quantization + "
         f"dequantized GEMM with its sum|a||b| bound, {dt:.1f} s; FLOP counted as 2*rows*N*K",
     }
+
+
+def percentiles(v):
+    """p10, median and p90 of a list of per-launch times (ms)."""
+    v = sorted(v)
+    at = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]  # noqa: E731
+    return [round(at(0.1), 4), round(at(0.5), 4), round(at(0.9), 4)]
+
+
+def cold_steps(torch, dev, fns, reps):
+    """The step with cold caches: before each rep a 1 GiB scratch write
+    evicts the L2s and the 256 MB Infinity Cache, then the step's kernels
+    run between HIP events. Returns per-step median ms and p10/p50/p90 of
+    the step and of its last kernel (the GEMM)."""
+    scratch = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    steps, last = [], []
+    for r in range(reps + 1):
+        scratch.fill_(r & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        if r == 0:
+            continue  # the first rep warms the launch path
+        steps.append(ev[0].elapsed_time(ev[-1]))
+        last.append(ev[-2].elapsed_time(ev[-1]))
+    del scratch
+    return {"step_ms_p10_p50_p90": percentiles(steps), "gemm_ms_p10_p50_p90": percentiles(last), "reps": reps,
+            "evict": "1 GiB device write before each rep"}
 
 
 def mfma_probe(torch, mx, dev, a_codes, b_codes, iters=2000, reps=10):
@@ -494,11 +527,15 @@ def main():
         rm_total, (rq_ms, rg_ms) = timed_step(torch, rowmajor, 10, 2)
         _, (f_ms,) = timed_step(torch, [fused], 10, 2)
         fa = mean(f_ms)
+        cold = cold_steps(torch, dev, [quant, gemm], 10)
         out["extra"] = {
             "quantize_act_ms": round(qa, 4),
             "quantize_act_GBps": round(act_bytes / (qa * 1e-3) / 1e9, 1),
             "quantize_act_hbm_frac": round(act_bytes / (qa * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "gemm_ms": round(gemm_ms, 4),
+            "gemm_ms_p10_p50_p90": percentiles(g_ms),
+            "step_ms_p10_p50_p90": percentiles([a + b for a, b in zip(q_ms, g_ms)]),
+            "cold": cold,
             "linear_ws_one_call_ms": round(oc_total / 10, 4),
             "rowmajor_step_ms": round(rm_total / 10, 4),
             "rowmajor_step_TFLOPs": round(flop / (rm_total / 10 * 1e-3) / 1e12, 2),
