@@ -29,8 +29,9 @@ Prints ONE JSON line. Besides the contract fields it carries
                 quantizer's bandwidth, the same step on
                 row-major operands (mx_quantize_act + mx_linear_q), the
                 fused-prologue path (mx_linear), the weight quantizer, the
-                other Wan2.2 linears, and one whole denoise step's 400
-                linears (40 blocks) back to back.
+                other Wan2.2 linears, one whole denoise step's 400 linears
+                (40 blocks) back to back, and one GPU's share of a two-way
+                tensor-parallel split of four linears.
 
 Modes for profiling: --profile step|rowmajor|fused runs only those kernels
 (steps times, no oracle); --profile workloads runs the other workloads (FFN
@@ -389,6 +390,38 @@ def per_channel_step(torch, mx, synth, dev, M, K, N, steps=10, warmup=3):
     return res
 
 
+def tp2_shares(torch, mx, synth, dev, steps=10, warmup=3):
+    """One GPU's share of a two-way tensor-parallel split, at its real shape:
+    column-parallel halves of N (the q|k|v projection 75348x5120x7680 and the
+    FFN up-projection 75348x5120x6912 with GELU) and row-parallel halves of K
+    (attention out 75348x2560x5120 and FFN down 75348x6912x5120, bf16 partial
+    sums without the bias, which the all-reduce's owner would add). Each
+    share quantizes its own activations (rank-local) and runs the slab GEMM.
+    The exchange itself (an all-reduce of the row-parallel partials over
+    xGMI) is not measured: one GPU."""
+    M = 75348
+    shares = [("qkv column half", M, 5120, 7680, False, True), ("ffn up column half", M, 5120, 6912, True, True),
+              ("attn out row half", M, 2560, 5120, False, False), ("ffn down row half", M, 6912, 5120, False, False)]
+    res = {}
+    for i, (name, m, k, n, gelu, has_bias) in enumerate(shares):
+        x = synth.make_activation_device(m, k, 700 + i, dev)
+        w = mx.mx_quantize_weight_slab(synth.make_weight_device(n, k, 700 + i, dev))
+        b = synth.make_bias(n, 700 + i).to(dev) if has_bias else None
+        xs = mx.mx_quantize_act_slab(x)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        total, (q_ms, g_ms) = timed_step(
+            torch, [lambda: mx.mx_quantize_act_slab(x, xs), lambda: mx.mx_linear_slab(xs, w, b, gelu=gelu, y=y)],
+            steps, warmup)
+        ms = total / steps
+        flop = 2.0 * m * n * k
+        res[name] = {"shape": f"{m}x{k}x{n}" + (" gelu" if gelu else "") + ("" if has_bias else " no bias"),
+                     "ms": round(ms, 4), "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
+                     "gemm_TFLOPs": round(flop / (mean(g_ms) * 1e-3) / 1e12, 2)}
+        del x, w, xs, y
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -551,6 +584,7 @@ def main():
         out["extra"]["other_workloads"] = other_workloads(torch, mx, synth, dev)
         out["extra"]["denoise_step"] = denoise_step(torch, synth, dev)
         out["extra"]["per_channel_fp8"] = per_channel_step(torch, mx, synth, dev, M, K, N)
+        out["extra"]["tp2_shares"] = tp2_shares(torch, mx, synth, dev)
 
     if not args.no_cpu_baseline:
         del x, xsl, rowmajor
