@@ -89,8 +89,9 @@ const char* mx_last_error_message(void);
 int mx_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
                     uint8_t* q, uint8_t* s, void* stream);
 
-/* Weight quantization, the same rule ("weights are stored as FP8 E4M3 with
- * per-32 E8M0 scales"). w: [N][ldw] of type wdtype (MX_DT_F32 or MX_DT_BF16),
+/* Weight quantization by the same rule: the model card keeps its weights as
+ * E4M3 codes with one E8M0 scale for each 32 along K (section "Quantization
+ * Details"). w: [N][ldw] of type wdtype (MX_DT_F32 or MX_DT_BF16),
  * ldw >= K, ldw * sizeof(element) % 16 == 0; q: uint8 [N][K]; s: uint8 [N][K/32]. */
 int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
                        uint8_t* q, uint8_t* s, void* stream);

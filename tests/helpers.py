@@ -141,6 +141,12 @@ def assert_chain_close(y_gpu, y_star_up, S_up, epilogue_up, w2q, w2s, b2, what="
     allow = delta @ np.abs(oracle.dequantize_mx(w2q, w2s)).T
     y = f64(y_gpu) if isinstance(y_gpu, torch.Tensor) else np.asarray(y_gpu)
     err = np.abs(y - y2)
+    # The GPU multiplies codes whose values differ from the oracle's by at
+    # most delta, so its exact sum z is within `allow` of y2 and its error
+    # scale is at most S2 + allow. The usual bound on the GPU's rounding of z,
+    # 1e-3 (S2 + allow) + ulp(|z|), plus |z - y2| <= allow gives the
+    # tolerance below: `allow` enters once as the shift of the exact value;
+    # inside the tolerance it only widens S and the ulp's argument.
     tol = oracle.tolerance(S2 + allow, np.abs(y2) + allow) + allow
     bad = err > tol
     if bad.any():
