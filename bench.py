@@ -57,6 +57,19 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_qkv_75348x5120x15360.json")
 GEMM_SOURCES = ["mx_gemm.hip", "mx_device.h"]
 CPU_SAMPLE_ROWS = 8192
+# The pages' own figures, quoted with their setups (context only: other
+# hardware and software, not targets).
+CONTEXT = {
+    "quantized_weights_GiB_per_transformer": 13.99,
+    "quantized_weights_source": "model card 'Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)', "
+                                "Quantization Details (E4M3 weights + E8M0 scales of the 400 quantized linears; "
+                                "the shape arithmetic here gives 13.49 GiB)",
+    "mlx_gen_q8_s": 217.4,
+    "mlx_gen_bf16_s": 95.48,
+    "mlx_gen_setup": "'Planned: Wan quantization and motion parity', Current code reality: MLX-Gen q8 against "
+                     "BF16, 704x384, 25 frames, 12 steps, on that project's local Apple-MLX machine (the q8 format "
+                     "is not MXFP8)",
+}
 
 
 def kernel_source_hash():
@@ -273,26 +286,32 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
         outs = [torch.empty((shp.M, shp.N), dtype=torch.bfloat16, device=dev) for shp, _, _ in layers]
         slabs = [mx.mx_quantize_act_slab(acts[li] if acts[li] is not None else outs[li - 1])
                  for li in range(len(layers))]
-        # Per-shape kernel: the default plan (few-token kernel up to 256
+        # Each linear is one mx_linear call (quantizer + GEMM through the
+        # shape's plan). Plans: the default rule (few-token kernel up to 256
         # tokens, split-K while the 256 x 256 tiles leave CUs idle, else the
         # slab GEMM), then warm-up tuning on the real operands of each linear
-        # (mx_linear_tune times the candidate kernels and caches the fastest);
-        # the timed step runs the tuned plans.
-        plans = [mx.plan_linear(shp.M, shp.K, shp.N) for shp, _, _ in layers]
-        wss = [torch.empty((max(mx.mx_linear_tune_ws_bytes(shp.M, shp.K, shp.N), 1),), dtype=torch.uint8, device=dev)
+        # (mx_linear_tune times the candidate kernels on the quantized slab
+        # and caches the fastest); the timed step runs the tuned plans.
+        default_plans = [mx.plan_linear(shp.M, shp.K, shp.N) for shp, _, _ in layers]
+        wss = [torch.empty((max(mx.mx_linear_ws_bytes(shp.M, shp.K, shp.N), 1),), dtype=torch.uint8, device=dev)
                for shp, _, _ in layers]
 
         def run():
             for li, (shp, w, b) in enumerate(layers):
                 x = acts[li] if acts[li] is not None else outs[li - 1]
-                mx.mx_quantize_act_slab(x, slabs[li])
-                mx.mx_linear_slab_planned(plans[li], slabs[li], w, b, gelu=shp.gelu, y=outs[li], workspace=wss[li])
+                mx.mx_linear(x, w, b, gelu=shp.gelu, y=outs[li], workspace=wss[li])
 
-        run()
-        default_plans = list(plans)
         for li, (shp, w, b) in enumerate(layers):
+            x = acts[li] if acts[li] is not None else outs[li - 1]
+            if li > 0 and acts[li] is None:
+                run()  # the previous layer's output is this one's input
+            mx.mx_quantize_act_slab(x, slabs[li])
             if shp.M <= 4096:  # the large shapes' plan is the slab GEMM; tuning them takes seconds
-                plans[li] = mx.mx_linear_tune(slabs[li], w, b, gelu=shp.gelu, y=outs[li], workspace=wss[li], reps=5)
+                tws = torch.empty((max(mx.mx_linear_tune_ws_bytes(shp.M, shp.K, shp.N), 1),), dtype=torch.uint8,
+                                  device=dev)
+                mx.mx_linear_tune(slabs[li], w, b, gelu=shp.gelu, y=outs[li], workspace=tws, reps=5)
+                del tws
+        plans = [mx.plan_lookup(shp.M, shp.K, shp.N, shp.gelu) for shp, _, _ in layers]
         run()
 
         total, _ = timed_step(torch, [run], steps, warmup)
@@ -345,6 +364,8 @@ def denoise_step(torch, synth, dev, steps=2, warmup=1):
         step.set_block(block, w, b)
         del w, b
     inputs = synth.make_denoise_inputs(dev, on_device=True)
+    defaults = step.plans()
+    plans = step.tune(inputs)  # warm-up tuning of the block's one-call shapes, cached for the run
     total, _ = timed_step(torch, [lambda: step.run(inputs)], steps, warmup)
     ms = total / steps
     flop = step.flop()
@@ -357,6 +378,8 @@ def denoise_step(torch, synth, dev, steps=2, warmup=1):
         "ms": round(ms, 3),
         "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
         "pct_of_mxfp8_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 2),
+        "plans": {g: f"{k}{sp}" + ("" if (k, sp) == defaults[g] else f" (tuned; default {defaults[g][0]}{defaults[g][1]})")
+                  for g, (k, sp) in plans.items()},
     }
     del step, inputs
     torch.cuda.empty_cache()
@@ -487,7 +510,7 @@ def main():
         wq, ws = mx.mx_quantize_weight(w)
         xq, xs = mx.mx_quantize_act(x)
         rowmajor = [lambda: mx.mx_quantize_act(x, xq, xs), lambda: mx.mx_linear_q(xq, xs, wq, ws, bias, y=y)]
-        fused = lambda: mx.mx_linear(x, wq, ws, bias, y=y)  # noqa: E731
+        fused = lambda: mx.mx_linear_fused(x, wq, ws, bias, y=y)  # noqa: E731
     del w
 
     if args.profile:
@@ -530,7 +553,8 @@ def main():
             "M": M,
             "K": K,
             "N": N,
-            "step": "mx_quantize_act_slab + mx_linear_slab (bias, bf16 out); the two kernels of mx_linear_ws",
+            "step": "mx_quantize_act_slab + mx_linear_slab (bias, bf16 out): the two kernels mx_linear runs for "
+                    "this shape (its slab plan), timed one by one",
             "pct_of_mxfp8_peak": round(100.0 * value / PEAK_MXFP8_TFLOPS, 2),
         },
         "roofline": {
@@ -553,8 +577,8 @@ def main():
         act_bytes = M * K * (2 + 1 + 1 / 32)
         w_bytes = N * K * (4 + 1 + 1 / 32)
         wqa = mean(wq_per[0])
-        ws_buf = torch.empty((mx.mx_linear_ws_bytes(M, K),), dtype=torch.uint8, device=dev)
-        one_call = lambda: mx.mx_linear_ws(x, wsl, bias, y=y, workspace=ws_buf)  # noqa: E731
+        ws_buf = torch.empty((mx.mx_linear_ws_bytes(M, K, N),), dtype=torch.uint8, device=dev)
+        one_call = lambda: mx.mx_linear(x, wsl, bias, y=y, workspace=ws_buf)  # noqa: E731
         oc_total, _ = timed_step(torch, [one_call], 10, 2)
         del ws_buf
         rm_total, (rq_ms, rg_ms) = timed_step(torch, rowmajor, 10, 2)
@@ -569,7 +593,7 @@ def main():
             "gemm_ms_p10_p50_p90": percentiles(g_ms),
             "step_ms_p10_p50_p90": percentiles([a + b for a, b in zip(q_ms, g_ms)]),
             "cold": cold,
-            "linear_ws_one_call_ms": round(oc_total / 10, 4),
+            "mx_linear_one_call_ms": round(oc_total / 10, 4),
             "rowmajor_step_ms": round(rm_total / 10, 4),
             "rowmajor_step_TFLOPs": round(flop / (rm_total / 10 * 1e-3) / 1e12, 2),
             "rowmajor_gemm_ms": round(mean(rg_ms), 4),
@@ -581,6 +605,7 @@ def main():
 
     if not args.no_extra:
         del y
+        out["extra"]["context_from_pages"] = CONTEXT
         out["extra"]["other_workloads"] = other_workloads(torch, mx, synth, dev)
         out["extra"]["denoise_step"] = denoise_step(torch, synth, dev)
         out["extra"]["per_channel_fp8"] = per_channel_step(torch, mx, synth, dev, M, K, N)

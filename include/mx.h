@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 10
+#define MX_ABI_VERSION 11
 
 typedef enum {
   MX_OK = 0,
@@ -96,16 +96,20 @@ int mx_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx,
 int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
                        uint8_t* q, uint8_t* s, void* stream);
 
-/* The MXFP8 W8A8 linear with the activation quantization fused into the
- * GEMM's prologue:
+/* The MXFP8 W8A8 linear on row-major weights with the activation
+ * quantization fused into the GEMM's prologue (each 256-token tile quantized
+ * in the kernel, once for every 256 weight rows, no workspace):
  *   y[m][n] = bf16_rne( epi( sum_k xhat[m][k] * what[n][k] + f32(bias[n]) ) )
  * with xhat the MX quantization of x (same rule as mx_quantize_act) and what
  * the dequantized weights (wq, ws). Products are exact, sums are FP32.
  * x: bf16 [M][K]; wq: uint8 [N][K]; ws: uint8 [N][K/32]; bias: f16 [N] or
- * NULL; epilogue: mx_epilogue; y: bf16 [M][N]. */
-int mx_linear(const void* x, int64_t M, int64_t K,
-              const uint8_t* wq, const uint8_t* ws, int64_t N,
-              const void* bias, int epilogue, void* y, void* stream);
+ * NULL; epilogue: mx_epilogue; y: bf16 [M][N]. Correct for any K % 32 == 0
+ * but slow: its kernel holds the bf16 token tile beside 256 accumulators per
+ * lane and spills (about 240 TFLOP/s at 75348 x 5120 x 15360, against about
+ * 2700 for mx_linear). Kept for callers without slab weights or workspace. */
+int mx_linear_fused(const void* x, int64_t M, int64_t K,
+                    const uint8_t* wq, const uint8_t* ws, int64_t N,
+                    const void* bias, int epilogue, void* y, void* stream);
 
 /* The same linear on activations already quantized (e.g. by
  * mx_quantize_act): xq: uint8 [M][K], xs: uint8 [M][K/32]. */
@@ -165,27 +169,6 @@ int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
 int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                            const uint8_t* wq, const uint8_t* ws, int64_t N,
                            const void* bias, int epilogue, uint8_t* hq, uint8_t* hs, void* stream);
-
-/* Bytes of workspace mx_linear_ws needs for M token rows and reduction
- * length K: the activation slab, RM * K codes + RM * K / 32 scales with
- * RM = mx_slab_rows(M), rounded up to 256 bytes. -1 if M < 0 or K is not a
- * positive multiple of 64. */
-int64_t mx_linear_ws_bytes(int64_t M, int64_t K);
-
-/* The MXFP8 W8A8 linear in one call on the fast path, activation
- * quantization included: x bf16 [M][ldx] (ldx >= K, ldx % 8 == 0) is
- * quantized into `workspace` (its slab layout, mx_quantize_act_slab), then
- * multiplied by the slab-layout weights wq [K/64][RN][64], ws [K/64][RN][2]
- * (from mx_quantize_weight_slab or mx_slab_pack) with bias and epilogue into
- * y bf16 [M][N] (mx_linear_slab). Two kernels on `stream`; nothing is
- * allocated. workspace: device memory of at least mx_linear_ws_bytes(M, K)
- * bytes, 256-byte aligned, not overlapping x, the weights, bias or y; it is
- * overwritten. K % 64 == 0. Same results as mx_linear on the same weights
- * (bit for bit, when K % 128 == 0). */
-int mx_linear_ws(const void* x, int64_t M, int64_t K, int64_t ldx,
-                 const uint8_t* wq, const uint8_t* ws, int64_t N,
-                 const void* bias, int epilogue, void* y,
-                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Split-K for few token tiles. With M of a few hundred tokens (the 128-token
@@ -319,6 +302,44 @@ int mx_linear_slab_auto(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t
 
 /* Empties the plan cache. */
 void mx_linear_plan_clear(void);
+
+/* ------------------------------------------------------------------------
+ * The linear in one call: the production entry point. What the model card
+ * "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)" describes in
+ * "Quantization Details" for each of its quantized linears: bf16 activations
+ * quantized to MXFP8 at run time, multiplied against E4M3 weights with
+ * per-32 E8M0 scales, F16 bias; FP32 accumulation, bf16 output:
+ *   y[m][n] = bf16_rne( epi( sum_k xhat[m][k] * what[n][k] + f32(bias[n]) ) )
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace mx_linear needs for an M x K x N linear: the activation
+ * slab (mx_slab_rows(M) * K * 33 / 32), the few-token kernel's tile counters
+ * and the partial sums of any plan mx_linear_tune may pick for the shape,
+ * each rounded up to 256 bytes. 0 for M = 0 or N = 0; -1 on a bad shape (K
+ * not a positive multiple of 64, sizes past the limits). */
+int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N);
+
+/* x bf16 [M][ldx] (ldx >= K, ldx % 8 == 0) is quantized into `workspace`
+ * (mx_quantize_act_slab's layout), then multiplied by the slab weights
+ * wq [K/64][RN][64], ws [K/64][RN][2] (mx_quantize_weight_slab or
+ * mx_slab_pack) with bias (f16 [N] or NULL) and epilogue into y bf16 [M][N],
+ * through the shape's plan (mx_linear_plan_lookup: tuned if mx_linear_tune
+ * ran for it, else the default rule; a tuned plan that needs more workspace
+ * than given gives way to the default one). The few-token plan with several
+ * K ranges adds its partial sums inside the GEMM kernel (the workgroup
+ * finishing a tile last reduces it, in range order), so the call is two
+ * kernels on `stream` for the slab and few-token plans, three for split-K
+ * and balanced ones. Nothing is allocated. workspace: device memory of
+ * mx_linear_ws_bytes(M, K, N) bytes (at least what the chosen plan needs),
+ * 256-byte aligned, not overlapping x, the weights, bias or y; its contents
+ * are overwritten and need no initial value. K % 64 == 0, N % 16 == 0.
+ * Results: deterministic; bit-identical to mx_quantize_act_slab +
+ * mx_linear_slab_plan with the same plan. Errors: as mx_linear_slab, plus
+ * MX_ERR_INVALID_ARGUMENT for a bad pitch, a short or misplaced workspace. */
+int mx_linear(const void* x, int64_t M, int64_t K, int64_t ldx,
+              const uint8_t* wq, const uint8_t* ws, int64_t N,
+              const void* bias, int epilogue, void* y,
+              void* workspace, int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement. The MFMA peak that the 5.0 PFLOP/s figure assumes needs the

@@ -42,7 +42,7 @@ SIGNATURES = {
     "mx_last_error_message": ([], ctypes.c_char_p),
     "mx_quantize_act": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_quantize_weight": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
-    "mx_linear": ([_P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
+    "mx_linear_fused": ([_P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_linear_q": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_slab_rows": ([_I64], _I64),
     "mx_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
@@ -50,8 +50,6 @@ SIGNATURES = {
     "mx_slab_pack": ([_P, _P, _I64, _I64, _P, _P, _P], _INT),
     "mx_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_linear_slab_requant": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _P], _INT),
-    "mx_linear_ws_bytes": ([_I64, _I64], _I64),
-    "mx_linear_ws": ([_P, _I64, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "mx_linear_splitk_ws_bytes": ([_I64, _I64, _INT], _I64),
     "mx_linear_splitk_choose": ([_I64, _I64, _I64], _INT),
     "mx_linear_slab_splitk": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _INT, _P, _I64, _P], _INT),
@@ -68,6 +66,8 @@ SIGNATURES = {
     "mx_linear_plan_lookup": ([_I64, _I64, _I64, _INT, _PI, _PI], _INT),
     "mx_linear_slab_auto": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "mx_linear_plan_clear": ([], None),
+    "mx_linear_ws_bytes": ([_I64, _I64, _I64], _I64),
+    "mx_linear": ([_P, _I64, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
     "mx_probe_mfma": ([_P, _P, _I64, _INT, _INT, _P, _P], _INT),
     "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
@@ -194,16 +194,17 @@ def _linear_common(M, K, wq, ws, bias, y, dev):
     return N, y
 
 
-def mx_linear(x, wq, ws, bias=None, gelu=False, y=None):
-    """y = bf16(epi(quant_mx(x) @ dequant(wq, ws)^T + bias)), activation
-    quantization fused into the GEMM. x: bf16 [M, K]."""
+def mx_linear_fused(x, wq, ws, bias=None, gelu=False, y=None):
+    """y = bf16(epi(quant_mx(x) @ dequant(wq, ws)^T + bias)) on row-major
+    weights, activation quantization fused into the GEMM's prologue (slow:
+    see mx.h). x: bf16 [M, K]."""
     dev = x.device
     _need(x, "x", torch.bfloat16, dev)
     M, K = x.shape
     N, y = _linear_common(M, K, wq, ws, bias, y, dev)
     epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
     with torch.cuda.device(dev):
-        _check(lib().mx_linear(_ptr(x), M, K, _ptr(wq), _ptr(ws), N, _ptr(bias), epi, _ptr(y), _stream(dev)))
+        _check(lib().mx_linear_fused(_ptr(x), M, K, _ptr(wq), _ptr(ws), N, _ptr(bias), epi, _ptr(y), _stream(dev)))
     return y
 
 
@@ -356,49 +357,6 @@ def mx_linear_slab_requant(x, w, bias=None, gelu=False, out=None):
             )
         )
     return out
-
-
-def mx_linear_ws_bytes(M, K):
-    return lib().mx_linear_ws_bytes(M, K)
-
-
-def mx_linear_ws(x, w, bias=None, gelu=False, y=None, workspace=None):
-    """One call on the fast path: bf16 x [M, K] (rows may be strided) is
-    quantized into `workspace` (uint8, >= mx_linear_ws_bytes(M, K) bytes;
-    allocated here when None) and multiplied by the slab weights w."""
-    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
-    dev = x.device
-    M, K = x.shape
-    _need(w.q, "w.q", torch.uint8, dev)
-    _need(w.s, "w.s", torch.uint8, dev)
-    if w.K != K:
-        raise ValueError(f"x has K = {K}, w has K = {w.K}")
-    N = w.rows
-    if bias is not None:
-        _need(bias, "bias", torch.float16, dev)
-        if bias.shape != (N,):
-            raise ValueError("bias must be f16 [N]")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
-    _need(y, "y", torch.bfloat16, dev)
-    if y.shape != (M, N):
-        raise ValueError("y must be bf16 [M, N]")
-    need = mx_linear_ws_bytes(M, K)
-    if need < 0:
-        raise ValueError("the slab layout needs K % 64 == 0")
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, dev)
-    ld = x.stride(0) if M > 1 else K
-    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
-    with torch.cuda.device(dev):
-        _check(
-            lib().mx_linear_ws(
-                _ptr(x), M, K, ld, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _ptr(workspace),
-                workspace.numel(), _stream(dev),
-            )
-        )
-    return y
 
 
 def mx_linear_splitk_ws_bytes(M, N, splits):
@@ -704,6 +662,50 @@ def mx_pc_linear_slab(x, w, bias=None, gelu=False, y=None):
         _check(
             lib().mx_pc_linear_slab(
                 _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _stream(dev)
+            )
+        )
+    return y
+
+
+def mx_linear_ws_bytes(M, K, N):
+    return lib().mx_linear_ws_bytes(M, K, N)
+
+
+def mx_linear(x, w, bias=None, gelu=False, y=None, workspace=None):
+    """The linear in one call (mx.h mx_linear): bf16 x [M, K] (rows may be
+    strided) is quantized into `workspace` and multiplied by the slab weights
+    w through the shape's plan (tuned or default). workspace: uint8 of at
+    least mx_linear_ws_bytes(M, K, N) bytes, allocated here when None."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    dev = x.device
+    M, K = x.shape
+    _need(w.q, "w.q", torch.uint8, dev)
+    _need(w.s, "w.s", torch.uint8, dev)
+    if w.K != K:
+        raise ValueError(f"x has K = {K}, w has K = {w.K}")
+    N = w.rows
+    if bias is not None:
+        _need(bias, "bias", torch.float16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be f16 [N]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    need = mx_linear_ws_bytes(M, K, N)
+    if need < 0:
+        raise ValueError("the slab layout needs K % 64 == 0")
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    ld = x.stride(0) if M > 1 else K
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(
+            lib().mx_linear(
+                _ptr(x), M, K, ld, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _ptr(workspace),
+                workspace.numel(), _stream(dev),
             )
         )
     return y

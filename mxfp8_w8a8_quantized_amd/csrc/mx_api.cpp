@@ -194,6 +194,28 @@ int check_pc_quantize(const void* x, int dt, int64_t rows, int64_t K, int64_t ld
   return check_device();
 }
 
+// Shape limits of the few-token kernel: it addresses a tile's K range with
+// 32-bit offsets that run a few slabs past it, and launches tiles x splits
+// workgroups.
+int check_small_shape(int64_t M, int64_t K, int64_t N, int splits) {
+  const int64_t span = K / 64 + 16;
+  if (span * mx::slab_rows(M) * 64 >= (int64_t(1) << 31) || span * mx::slab_rows(N) * 64 >= (int64_t(1) << 31))
+    return fail(MX_ERR_UNSUPPORTED, "(K/64 + 16) * 64 * rows must be below 2^31 for M and N (M = %lld, N = %lld)",
+                (long long)M, (long long)N);
+  const int64_t tiles = mx::small_tiles(M, N);
+  if (tiles * splits > kMaxSplitWorkgroups)
+    return fail(MX_ERR_UNSUPPORTED, "%lld tiles x %d splits exceed 2^24 workgroups", (long long)tiles, splits);
+  return MX_OK;
+}
+
+// Split-K on 256 x 256 tiles launches tiles x splits workgroups.
+int check_splitk_shape(int64_t M, int64_t N, int splits) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles * splits > kMaxSplitWorkgroups)
+    return fail(MX_ERR_UNSUPPORTED, "%lld tiles x %d splits exceed 2^24 workgroups", (long long)tiles, splits);
+  return MX_OK;
+}
+
 // Compute units of the current device (the balanced GEMM's round size).
 int cu_count() {
   int dev = 0, n = 0;
@@ -279,8 +301,8 @@ int mx_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, ui
   return finish(mx::launch_slab_pack(q, s, rows, K, qslab, sslab, (hipStream_t)stream), "slab pack launch");
 }
 
-int mx_linear(const void* x, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws, int64_t N, const void* bias,
-              int epilogue, void* y, void* stream) {
+int mx_linear_fused(const void* x, int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws, int64_t N,
+                    const void* bias, int epilogue, void* y, void* stream) {
   int st = check_linear_common(M, K, wq, ws, N, bias, epilogue, y);
   if (st != MX_OK || M == 0 || N == 0) return st;
   if (x == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x");
@@ -339,47 +361,6 @@ int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int6
                 "linear launch");
 }
 
-int64_t mx_linear_ws_bytes(int64_t M, int64_t K) {
-  if (M < 0 || K <= 0 || K % 64 != 0 || K > kMaxKN || M > kMaxRows) return -1;
-  const int64_t RM = mx::slab_rows(M);
-  const int64_t bytes = RM * K + RM * (K / 32);
-  return (bytes + 255) / 256 * 256;
-}
-
-int mx_linear_ws(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws, int64_t N,
-                 const void* bias, int epilogue, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
-  // The token slab lives in the workspace: check it as the operand it becomes.
-  const uint64_t RM0 = M > 0 && M <= kMaxRows ? (uint64_t)mx::slab_rows(M) : 0;
-  const uint8_t* wxq = (const uint8_t*)workspace;
-  const uint8_t* wxs = workspace != nullptr && K > 0 ? wxq + RM0 * (uint64_t)K : nullptr;
-  int st = check_linear_slab(wxq, wxs, M, K, wq, ws, N, bias, epilogue);
-  if (st != MX_OK || M == 0 || N == 0) return st;
-  if (x == nullptr || y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x, y or workspace");
-  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
-    return fail(MX_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, workspace 256-byte aligned");
-  const int64_t need = mx_linear_ws_bytes(M, K);
-  if (workspace_bytes < need)
-    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
-  const uint64_t RM = (uint64_t)mx::slab_rows(M), RN = (uint64_t)mx::slab_rows(N);
-  uint8_t* xq = (uint8_t*)workspace;
-  uint8_t* xs = xq + RM * K;
-  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2, ybytes = (uint64_t)M * N * 2;
-  if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, y, ybytes) ||
-      overlap(workspace, need, wq, RN * K) || overlap(workspace, need, ws, RN * (K / 32)) ||
-      overlap(workspace, need, bias, (uint64_t)N * 2))
-    return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
-  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, wq, RN * K) || overlap(y, ybytes, ws, RN * (K / 32)) ||
-      overlap(y, ybytes, bias, (uint64_t)N * 2))
-    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
-  if ((st = check_device()) != MX_OK) return st;
-  (void)hipGetLastError();
-  hipError_t e = mx::launch_quantize_slab(0, x, M, K, ldx, xq, xs, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "quantize launch");
-  return finish(mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, (hipStream_t)stream),
-                "linear launch");
-}
-
 int64_t mx_linear_splitk_ws_bytes(int64_t M, int64_t N, int splits) {
   if (M < 0 || N < 0 || M > kMaxRows || N > kMaxKN || splits < 1 || splits > kMaxKN / 64) return -1;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -407,9 +388,7 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
   if (y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL y or workspace");
   if (!aligned(y, 16) || !aligned(workspace, 256))
     return fail(MX_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned, workspace 256-byte aligned");
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles * splits > kMaxSplitWorkgroups)
-    return fail(MX_ERR_UNSUPPORTED, "%lld tiles x %d splits exceed 2^24 workgroups", (long long)tiles, splits);
+  if ((st = check_splitk_shape(M, N, splits)) != MX_OK) return st;
   const int64_t need = mx_linear_splitk_ws_bytes(M, N, splits);
   if (workspace_bytes < need)
     return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
@@ -448,15 +427,7 @@ int mx_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_
   if (M == 0 || N == 0) return MX_OK;
   if (y == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL y");
   if (!aligned(y, 16)) return fail(MX_ERR_INVALID_ARGUMENT, "y must be 16-byte aligned");
-  // The kernel addresses a tile's K range with 32-bit offsets that run a few
-  // slabs past it.
-  const int64_t span = K / 64 + 16;
-  if (span * mx::slab_rows(M) * 64 >= (int64_t(1) << 31) || span * mx::slab_rows(N) * 64 >= (int64_t(1) << 31))
-    return fail(MX_ERR_UNSUPPORTED, "(K/64 + 16) * 64 * rows must be below 2^31 for M and N (M = %lld, N = %lld)",
-                (long long)M, (long long)N);
-  const int64_t tiles = mx::small_tiles(M, N);
-  if (tiles * splits > kMaxSplitWorkgroups)
-    return fail(MX_ERR_UNSUPPORTED, "%lld tiles x %d splits exceed 2^24 workgroups", (long long)tiles, splits);
+  if ((st = check_small_shape(M, K, N, splits)) != MX_OK) return st;
   const int64_t need = mx_linear_small_ws_bytes(M, N, splits);
   const uint64_t ybytes = (uint64_t)M * N * 2;
   if ((st = check_slab_output(xq, xs, M, K, wq, ws, N, bias, y, ybytes, "y")) != MX_OK) return st;
@@ -788,6 +759,130 @@ int mx_probe_mfma(const uint8_t* a, const uint8_t* b, int64_t bytes, int iters, 
 void mx_linear_plan_clear(void) {
   std::lock_guard<std::mutex> lock(g_plan_mutex);
   g_plans.clear();
+}
+
+}  // extern "C"
+
+/* ---- The one-call linear: quantize into the workspace, then the plan ---- */
+
+namespace {
+
+int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace layout of mx_linear: the activation slab (codes, then scales),
+// the few-token kernel's tile counters, the plan's partial sums.
+struct LinearWs {
+  int64_t act, counters, part;  // byte offsets
+};
+
+LinearWs linear_ws_layout(int64_t M, int64_t K, int64_t N) {
+  const int64_t RM = mx::slab_rows(M);
+  LinearWs L;
+  L.act = 0;
+  L.counters = round256(RM * K + RM * (K / 32));
+  L.part = L.counters + round256(mx::small_tiles(M, N) * 4);
+  return L;
+}
+
+// One linear on the slab operands in the workspace, by plan; the few-token
+// kernel reduces its K ranges in the kernel (counters cleared by the
+// quantizer). The shape checks of the plan's own entry point run first.
+int run_linear_plan(int kind, int splits, const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq,
+                    const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y, uint8_t* work,
+                    hipStream_t stream) {
+  const LinearWs L = linear_ws_layout(M, K, N);
+  const int64_t RM = mx::slab_rows(M);
+  uint8_t* xq = work + L.act;
+  uint8_t* xs = xq + RM * K;
+  uint32_t* counters = (uint32_t*)(work + L.counters);
+  float* part = (float*)(work + L.part);
+  int st = MX_OK;
+  if (kind == MX_PLAN_SMALL) st = check_small_shape(M, K, N, splits);
+  if (kind == MX_PLAN_SPLITK) st = check_splitk_shape(M, N, splits);
+  if (st != MX_OK) return st;
+  const bool fused_reduce = kind == MX_PLAN_SMALL && splits > 1;
+  hipError_t e = mx::launch_quantize_slab(0, x, M, K, ldx, xq, xs, stream, fused_reduce ? counters : nullptr,
+                                          fused_reduce ? (int)mx::small_tiles(M, N) : 0);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  switch (kind) {
+    case MX_PLAN_SLAB:
+      e = mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, stream);
+      break;
+    case MX_PLAN_SMALL:
+      e = mx::launch_linear_slab_small(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, part, stream,
+                                       fused_reduce ? counters : nullptr);
+      break;
+    case MX_PLAN_SPLITK:
+      e = mx::launch_linear_slab_splitk(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, part, stream);
+      break;
+    case MX_PLAN_BALANCED:
+      e = mx::launch_linear_slab_balanced(xq, xs, M, K, wq, ws, N, bias, epilogue, y, cu_count(), part, stream);
+      break;
+    default:
+      return fail(MX_ERR_INVALID_ARGUMENT, "unknown plan kind %d", kind);
+  }
+  return finish(e, "linear launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 0 || K < 64 || K % 64 != 0 || M > kMaxRows || N > kMaxKN || K > kMaxKN) return -1;
+  if (M == 0 || N == 0) return 0;
+  const int64_t part = mx_linear_tune_ws_bytes(M, K, N);  // the largest any candidate plan needs
+  if (part < 0) return -1;
+  return linear_ws_layout(M, K, N).part + round256(part);
+}
+
+int mx_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws, int64_t N,
+              const void* bias, int epilogue, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
+  // The token slab lives in the workspace: check it as the operand it becomes.
+  const uint64_t RM0 = M > 0 && M <= kMaxRows ? (uint64_t)mx::slab_rows(M) : 0;
+  const uint8_t* wxq = (const uint8_t*)workspace;
+  const uint8_t* wxs = workspace != nullptr && K > 0 ? wxq + RM0 * (uint64_t)K : nullptr;
+  int st = check_linear_slab(wxq, wxs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (x == nullptr || y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x, y or workspace");
+  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
+    return fail(MX_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, workspace 256-byte aligned");
+  // The activation slab and the counters come first in the workspace; the
+  // plan's partial sums follow.
+  const int64_t base = linear_ws_layout(M, K, N).part;
+  if (workspace_bytes < base)
+    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, at least %lld needed (mx_linear_ws_bytes gives %lld)",
+                (long long)workspace_bytes, (long long)base, (long long)mx_linear_ws_bytes(M, K, N));
+  const uint64_t RN = (uint64_t)mx::slab_rows(N);
+  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2, ybytes = (uint64_t)M * N * 2;
+  auto overlaps_args = [&](uint64_t nbytes) {
+    return overlap(workspace, nbytes, x, xbytes) || overlap(workspace, nbytes, y, ybytes) ||
+           overlap(workspace, nbytes, wq, RN * K) || overlap(workspace, nbytes, ws, RN * (K / 32)) ||
+           overlap(workspace, nbytes, bias, (uint64_t)N * 2);
+  };
+  if (overlaps_args((uint64_t)base)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
+  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, wq, RN * K) || overlap(y, ybytes, ws, RN * (K / 32)) ||
+      overlap(y, ybytes, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if ((st = check_device()) != MX_OK) return st;
+  // The plan: the tuned one cached for this shape, else the default rule; a
+  // tuned plan whose partial sums do not fit the workspace gives way to the
+  // default plan.
+  int kind, splits;
+  if ((st = mx_linear_plan_lookup(M, K, N, epilogue, &kind, &splits)) != MX_OK) return st;
+  int64_t need = base + round256(mx_linear_plan_ws_bytes(kind, splits, M, K, N));
+  if (need > workspace_bytes) {
+    if ((st = mx_linear_plan_default(M, K, N, &kind, &splits)) != MX_OK) return st;
+    need = base + round256(mx_linear_plan_ws_bytes(kind, splits, M, K, N));
+  }
+  if (workspace_bytes < need)
+    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed (mx_linear_ws_bytes gives %lld)",
+                (long long)workspace_bytes, (long long)need, (long long)mx_linear_ws_bytes(M, K, N));
+  if (overlaps_args((uint64_t)need)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
+  (void)hipGetLastError();
+  return run_linear_plan(kind, splits, x, M, K, ldx, wq, ws, N, bias, epilogue, y, (uint8_t*)workspace,
+                         (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -15,10 +15,11 @@ kernels behind the C ABI:
   text tokens (N = 2 * hidden). An output column depends only on its own weight
   row, so the concatenation changes no value; the outputs are column blocks
   of one bf16 tensor.
-* Each of those linears is one mx_linear_ws call: the activation is quantized
-  into the shared workspace slab, then multiplied by the slab weights. The
-  text-token GEMM (512 tokens: too few tiles to occupy the GPU) quantizes into
-  the same slab and runs split-K (mx_linear_slab_splitk).
+* Each of those linears is one mx_linear call: the activation is quantized
+  into the shared workspace slab, then multiplied by the slab weights through
+  the shape's plan (tuned by ``tune()`` on the block's real operands, else
+  the default rule: split-K for the 512 text tokens, whose 256 x 256 tiles
+  are too few to occupy the GPU, the slab GEMM for the video tokens).
 * The feed-forward pair quantizes its input into the workspace, runs
   ffn.net.0.proj with the requantizing epilogue (the MX slab of its bf16 GELU
   output, never written as bf16) and ffn.net.2 on that slab.
@@ -30,9 +31,8 @@ activation each linear reads, by input role (``ROLES``).
 
 import torch
 
-from . import Slab, mx_linear_slab, mx_linear_slab_requant, mx_linear_slab_splitk, mx_linear_splitk_choose
-from . import mx_linear_splitk_ws_bytes, mx_linear_ws, mx_linear_ws_bytes, mx_quantize_act_slab
-from . import mx_quantize_weight_slab, mx_slab_rows
+from . import Slab, mx_linear, mx_linear_slab, mx_linear_slab_requant, mx_linear_tune, mx_linear_tune_ws_bytes
+from . import mx_linear_ws_bytes, mx_quantize_act_slab, mx_quantize_weight_slab, mx_slab_rows, plan_lookup
 
 # Input role of each GEMM of a block, in call order, with the linears it
 # fuses (names as in the Wan2.2 transformer's state dict).
@@ -78,23 +78,15 @@ class DenoiseStepLinears:
             torch.empty((ffn // 64, mx_slab_rows(tokens), 2), dtype=torch.uint8, device=self.device),
             tokens,
         )
-        ws = max(mx_linear_ws_bytes(tokens, hidden), mx_linear_ws_bytes(text_tokens, hidden))
+        # One workspace for every one-call linear of a block: the activation
+        # slab first (also the feed-forward input, viewed as a slab below),
+        # then what the shape's plan needs.
+        ws = max(mx_linear_ws_bytes(M, K, N) for gemm, M, K, N, _ in self.shapes() if gemm != "ffn.net.2")
         if ws < 0:
             raise ValueError("hidden must be a multiple of 64")
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=self.device)
-        # The workspace viewed as an input slab, the layout mx_linear_ws gives
-        # it (codes, then scales): the feed-forward input, the text tokens.
         self.ffn_input = self._slab_view(tokens)
-        self.text_input = self._slab_view(text_tokens)
-        # Split counts per GEMM (1: mx_linear_ws) and the partial-sum workspace.
-        self.splits = {}
-        part = 0
-        for gemm, M, K, N, _ in self.shapes():
-            sp = mx_linear_splitk_choose(M, K, N) if gemm not in ("ffn.net.0.proj", "ffn.net.2") else 1
-            self.splits[gemm] = sp
-            if sp > 1:
-                part = max(part, mx_linear_splitk_ws_bytes(M, N, sp))
-        self.partials = torch.empty((part,), dtype=torch.uint8, device=self.device) if part else None
+        self.tuned = {}
 
     def _slab_view(self, rows):
         R = mx_slab_rows(rows)
@@ -158,13 +150,40 @@ class DenoiseStepLinears:
                 mx_linear_slab_requant(self.ffn_input, w, b, gelu=gelu, out=self.ffn_hidden)
             elif gemm == "ffn.net.2":
                 mx_linear_slab(self.ffn_hidden, w, b, gelu=gelu, y=self.outputs[gemm])
-            elif self.splits[gemm] > 1:
-                xs = self.text_input if role == "text" else self._slab_view(self.rows[role])
-                mx_quantize_act_slab(inputs[role], xs)
-                mx_linear_slab_splitk(xs, w, b, gelu=gelu, y=self.outputs[gemm], splits=self.splits[gemm],
-                                      workspace=self.partials)
             else:
-                mx_linear_ws(inputs[role], w, b, gelu=gelu, y=self.outputs[gemm], workspace=self.workspace)
+                mx_linear(inputs[role], w, b, gelu=gelu, y=self.outputs[gemm], workspace=self.workspace)
+
+    def tune(self, inputs, block=0, reps=5):
+        """Warm-up tuning (mx_linear_tune) of the one-call GEMMs of a block on
+        block `block`'s weights and the given inputs: each shape's candidate
+        kernels are timed once and the fastest is cached for the process, so
+        every later run() takes it. Synchronizes; returns {gemm: plan} with
+        the plan each GEMM runs from now on (its default where not tuned)."""
+        slabs = self.weights[block]
+        if slabs is None:
+            raise RuntimeError(f"block {block} has no weights (set_block)")
+        self._check_inputs(inputs)
+        tune_ws = None
+        for gemm, role, _, gelu in GEMMS:
+            if gemm in ("ffn.net.0.proj", "ffn.net.2"):
+                continue  # the requantizing pair runs the slab GEMM itself
+            w, b = slabs[gemm]
+            M, K, N = self.rows[role], self.hidden, w.rows
+            need = max(mx_linear_tune_ws_bytes(M, K, N), 1)
+            if tune_ws is None or tune_ws.numel() < need:
+                tune_ws = torch.empty((need,), dtype=torch.uint8, device=self.device)
+            xs = self._slab_view(M)
+            mx_quantize_act_slab(inputs[role], xs)
+            self.tuned[gemm] = mx_linear_tune(xs, w, b, gelu=gelu, y=self.outputs[gemm], workspace=tune_ws,
+                                              reps=reps)
+        del tune_ws
+        return self.plans()
+
+    def plans(self):
+        """{gemm: (kind, splits)} each one-call GEMM runs with (mx_linear's
+        plan lookup: tuned, else the default rule)."""
+        return {gemm: plan_lookup(M, K, N, gelu) for gemm, M, K, N, gelu in self.shapes()
+                if gemm not in ("ffn.net.0.proj", "ffn.net.2")}
 
     def run(self, inputs):
         """Enqueue the whole step: every block's linears, in block order."""

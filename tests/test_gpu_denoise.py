@@ -118,11 +118,15 @@ def test_denoise_step_shapes_and_flop():
     assert step.flop() == 2 * 2.0 * per_block
 
 
-def test_denoise_step_small_against_oracle():
+@pytest.mark.parametrize("tuned", [False, True])
+def test_denoise_step_small_against_oracle(tuned):
     # The same runner on a small model (2 blocks, 300 + 40 tokens, hidden
-    # 256, ffn 512): every output element of both blocks against the oracle.
+    # 256, ffn 512): every output element of both blocks against the oracle,
+    # with the default plans and after warm-up tuning of block 0's shapes
+    # (the plans tune() reports are the ones mx_linear then looks up).
     from mxfp8_w8a8_quantized_amd.denoise import GEMMS, DenoiseStepLinears
 
+    mx().mx_linear_plan_clear()
     d = dev()
     M, T, H, F = 300, 40, 256, 512
     step = DenoiseStepLinears(2, M, T, H, F, d)
@@ -140,6 +144,10 @@ def test_denoise_step_small_against_oracle():
     for role, seed in synth.DENOISE_ROLE_SEEDS.items():
         inputs[role] = synth.make_text_context(T, H, seed) if role == "text" else synth.make_activation(M, H, seed)
     inputs_d = {k: v.to(d) for k, v in inputs.items()}
+    if tuned:
+        plans = step.tune(inputs_d)
+        assert set(plans) == {g for g, _, _, _ in GEMMS} - {"ffn.net.0.proj", "ffn.net.2"}
+        assert plans == step.plans() and plans["attn2.kv"] == step.tuned["attn2.kv"]
     for block in range(2):
         step.run_block(block, inputs_d)
         torch.cuda.synchronize()

@@ -26,7 +26,7 @@ def run_case(M, K, N, seed, bias=True, gelu=False, fused=True, x=None):
     b = synth.make_bias(N, seed) if bias else None
     wq, ws = mx().mx_quantize_weight(w.to(d))
     if fused:
-        y = mx().mx_linear(x.to(d), wq, ws, None if b is None else b.to(d), gelu=gelu)
+        y = mx().mx_linear_fused(x.to(d), wq, ws, None if b is None else b.to(d), gelu=gelu)
     else:
         xq, xs = mx().mx_quantize_act(x.to(d))
         y = mx().mx_linear_q(xq, xs, wq, ws, None if b is None else b.to(d), gelu=gelu)
@@ -68,7 +68,7 @@ def test_fused_equals_prequantized_bitwise():
     w = synth.make_weight(512, 1024, seed=11).to(d)
     b = synth.make_bias(512, seed=11).to(d)
     wq, ws = mx().mx_quantize_weight(w)
-    y1 = mx().mx_linear(x, wq, ws, b, gelu=True)
+    y1 = mx().mx_linear_fused(x, wq, ws, b, gelu=True)
     xq, xs = mx().mx_quantize_act(x)
     y2 = mx().mx_linear_q(xq, xs, wq, ws, b, gelu=True)
     torch.cuda.synchronize()
@@ -86,7 +86,7 @@ def test_identity_weight_reproduces_quantized_input_bitwise():
     x = (x.double() * torch.from_numpy(np.exp2(rng.integers(-60, 60, size=(1000, 1))))).to(torch.bfloat16)
     eye = torch.eye(K, dtype=torch.float32)
     wq, ws = mx().mx_quantize_weight(eye.to(d))
-    y = mx().mx_linear(x.to(d), wq, ws)
+    y = mx().mx_linear_fused(x.to(d), wq, ws)
     xq, xs = mx().mx_quantize_act(x.to(d))
     y2 = mx().mx_linear_q(xq, xs, wq, ws)
     torch.cuda.synchronize()
@@ -114,8 +114,8 @@ def test_deterministic_and_fully_written():
     wq, ws = mx().mx_quantize_weight(w)
     y1 = torch.full((333, 768), float("nan"), dtype=torch.bfloat16, device=d)
     y2 = torch.full((333, 768), float("nan"), dtype=torch.bfloat16, device=d)
-    mx().mx_linear(x, wq, ws, y=y1)
-    mx().mx_linear(x, wq, ws, y=y2)
+    mx().mx_linear_fused(x, wq, ws, y=y1)
+    mx().mx_linear_fused(x, wq, ws, y=y2)
     torch.cuda.synchronize()
     assert not torch.isnan(y1).any()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
@@ -125,7 +125,7 @@ def test_empty_batch():
     d = dev()
     w = synth.make_weight(256, 128, seed=1).to(d)
     wq, ws = mx().mx_quantize_weight(w)
-    y = mx().mx_linear(torch.empty((0, 128), dtype=torch.bfloat16, device=d), wq, ws)
+    y = mx().mx_linear_fused(torch.empty((0, 128), dtype=torch.bfloat16, device=d), wq, ws)
     assert y.shape == (0, 256)
 
 
@@ -146,7 +146,7 @@ def test_workload_configs(cfg):
         b = synth.make_bias(shp.N, seed)
         wq, ws = mx().mx_quantize_weight(w.to(d))
         xd = x.to(d)
-        y = mx().mx_linear(xd, wq, ws, b.to(d), gelu=shp.gelu)
+        y = mx().mx_linear_fused(xd, wq, ws, b.to(d), gelu=shp.gelu)
         torch.cuda.synchronize()
         rows = np.arange(shp.M) if shp.M <= 512 else sampled_rows(shp.M)
         yref, S = oracle_linear(x[rows], w, b, shp.gelu)
@@ -167,8 +167,8 @@ def test_ffn_chain_requantizes_intermediate():
     w2, b2 = synth.make_weight(down.N, down.K, 8), synth.make_bias(down.N, 8)
     w1q, w1s = mx().mx_quantize_weight(w1.to(d))
     w2q, w2s = mx().mx_quantize_weight(w2.to(d))
-    h = mx().mx_linear(x.to(d), w1q, w1s, b1.to(d), gelu=True)
-    y = mx().mx_linear(h, w2q, w2s, b2.to(d))
+    h = mx().mx_linear_fused(x.to(d), w1q, w1s, b1.to(d), gelu=True)
+    y = mx().mx_linear_fused(h, w2q, w2s, b2.to(d))
     torch.cuda.synchronize()
     rows = sampled_rows(M, 64, seed=1)
     href, S1 = oracle_linear(x[rows], w1, b1, True)

@@ -105,19 +105,19 @@ def test_nonfinite_balanced_split_last_round():
     assert_linear_close(y, yref, S, what="balanced")
 
 
-@pytest.mark.parametrize("path", ["ws", "rowmajor", "fused"])
+@pytest.mark.parametrize("path", ["onecall", "rowmajor", "fused"])
 def test_nonfinite_groups_one_call_and_row_major(path):
     M, K, N = 300, 640, 272
     print(f"nonfinite {path} M={M} K={K} N={N}", flush=True)
     d = dev()
     x, w, b = poisoned(M, K, N, seed=47)
     xd, wd, bd = x.to(d), w.to(d), b.to(d)
-    if path == "ws":
-        y = mx().mx_linear_ws(xd, mx().mx_quantize_weight_slab(wd), bd)
+    if path == "onecall":
+        y = mx().mx_linear(xd, mx().mx_quantize_weight_slab(wd), bd)
     else:
         wq, wsc = mx().mx_quantize_weight(wd)
         if path == "fused":
-            y = mx().mx_linear(xd, wq, wsc, bd)
+            y = mx().mx_linear_fused(xd, wq, wsc, bd)
         else:
             xq, xsc = mx().mx_quantize_act(xd)
             y = mx().mx_linear_q(xq, xsc, wq, wsc, bd)

@@ -291,7 +291,7 @@ def test_linear_ws_one_call(M, K, N, gelu):
     b = synth.make_bias(N, seed=M + K)
     wsl = mx().mx_quantize_weight_slab(w.to(d))
     xd = base.to(d)[:, 32:32 + K]
-    y1 = mx().mx_linear_ws(xd, wsl, b.to(d), gelu=gelu)
+    y1 = mx().mx_linear(xd, wsl, b.to(d), gelu=gelu)
     y2 = mx().mx_linear_slab(mx().mx_quantize_act_slab(xd), wsl, b.to(d), gelu=gelu)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
@@ -444,9 +444,9 @@ def test_linear_ws_offsets_past_4gib():
     w, b = synth.make_weight(N, K, 61), synth.make_bias(N, 61)
     x = base.to(d).repeat((M + 999) // 1000, 1)[:M]
     wsl = mx().mx_quantize_weight_slab(w.to(d))
-    ws = torch.empty((mx().mx_linear_ws_bytes(M, K),), dtype=torch.uint8, device=d)
+    ws = torch.empty((mx().mx_linear_ws_bytes(M, K, N),), dtype=torch.uint8, device=d)
     assert ws.numel() > 1 << 32
-    y = mx().mx_linear_ws(x, wsl, b.to(d), workspace=ws)
+    y = mx().mx_linear(x, wsl, b.to(d), workspace=ws)
     torch.cuda.synchronize()
     rng = np.random.default_rng(8)
     rows = np.unique(np.concatenate([np.arange(3), np.arange(M - 80, M), rng.integers(0, M, 64),
