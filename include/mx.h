@@ -341,6 +341,25 @@ int mx_linear(const void* x, int64_t M, int64_t K, int64_t ldx,
               const void* bias, int epilogue, void* y,
               void* workspace, int64_t workspace_bytes, void* stream);
 
+/* mx_linear for callers that cannot allocate: code under HIP graph capture,
+ * serving loops that keep allocation out of their hot path, harnesses that
+ * forbid hipMalloc. The same linear, plan and results (bit for bit) as
+ * mx_linear, with no workspace argument: its workspace is a scratch array
+ * the library owns, 64 MiB of static device memory per GPU, held until the
+ * process ends; its device address is looked up once per device, on the
+ * first call. Limit: the activation slab, the tile counters and the plan's
+ * partial sums must fit in those 64 MiB (a tuned plan that does not fit gives
+ * way to the default plan first); larger shapes are MX_ERR_UNSUPPORTED
+ * (checked before anything is launched; e.g. up to about 12000 tokens at
+ * K = 5120). Every call on a GPU shares that GPU's array and leaves its
+ * contents behind (what must start at zero, the kernels clear themselves):
+ * calls that overlap in time on one GPU (several streams, concurrent graph
+ * replays) race and give wrong results, so serialise them. Nothing is
+ * allocated. Other errors: as mx_linear. */
+int mx_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx,
+                      const uint8_t* wq, const uint8_t* ws, int64_t N,
+                      const void* bias, int epilogue, void* y, void* stream);
+
 /* ------------------------------------------------------------------------
  * Measurement. The MFMA peak that the 5.0 PFLOP/s figure assumes needs the
  * full clock, which the chip does not hold when the matrix cores work on

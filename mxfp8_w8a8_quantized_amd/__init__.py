@@ -68,6 +68,7 @@ SIGNATURES = {
     "mx_linear_plan_clear": ([], None),
     "mx_linear_ws_bytes": ([_I64, _I64, _I64], _I64),
     "mx_linear": ([_P, _I64, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _P], _INT),
+    "mx_linear_noalloc": ([_P, _I64, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_probe_mfma": ([_P, _P, _I64, _INT, _INT, _P, _P], _INT),
     "mx_pc_quantize_act_slab": ([_P, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_pc_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
@@ -708,4 +709,34 @@ def mx_linear(x, w, bias=None, gelu=False, y=None, workspace=None):
                 workspace.numel(), _stream(dev),
             )
         )
+    return y
+
+
+def mx_linear_noalloc(x, w, bias=None, gelu=False, y=None):
+    """mx_linear with the library's own scratch array as its workspace (mx.h
+    mx_linear_noalloc: no workspace argument, nothing allocated by the
+    library; calls overlapping on one GPU race). y is allocated here when
+    None."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    dev = x.device
+    M, K = x.shape
+    _need(w.q, "w.q", torch.uint8, dev)
+    _need(w.s, "w.s", torch.uint8, dev)
+    if w.K != K:
+        raise ValueError(f"x has K = {K}, w has K = {w.K}")
+    N = w.rows
+    if bias is not None:
+        _need(bias, "bias", torch.float16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be f16 [N]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be bf16 [M, N]")
+    ld = x.stride(0) if M > 1 else K
+    epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
+    with torch.cuda.device(dev):
+        _check(lib().mx_linear_noalloc(_ptr(x), M, K, ld, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y),
+                                       _stream(dev)))
     return y

@@ -824,6 +824,70 @@ int run_linear_plan(int kind, int splits, const void* x, int64_t M, int64_t K, i
   return finish(e, "linear launch");
 }
 
+// mx_linear's checks and run. library_scratch: the workspace is the
+// library's own scratch array (mx_linear_noalloc; `workspace` is ignored and
+// the array's device address looked up after the host-side checks), so a
+// shape that needs more than it holds is MX_ERR_UNSUPPORTED rather than a
+// short workspace, and it cannot overlap the caller's buffers.
+int linear_one_call(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws, int64_t N,
+                    const void* bias, int epilogue, void* y, void* workspace, int64_t workspace_bytes, void* stream,
+                    bool library_scratch) {
+  // The token slab lives in the workspace: check it as the operand it
+  // becomes (any 256-aligned stand-in for the library's array).
+  if (library_scratch) workspace = (void*)(uintptr_t)256;
+  const uint64_t RM0 = M > 0 && M <= kMaxRows ? (uint64_t)mx::slab_rows(M) : 0;
+  const uint8_t* wxq = (const uint8_t*)workspace;
+  const uint8_t* wxs = workspace != nullptr && K > 0 ? wxq + RM0 * (uint64_t)K : nullptr;
+  int st = check_linear_slab(wxq, wxs, M, K, wq, ws, N, bias, epilogue);
+  if (st != MX_OK || M == 0 || N == 0) return st;
+  if (x == nullptr || y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x, y or workspace");
+  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
+    return fail(MX_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, workspace 256-byte aligned");
+  // The activation slab and the counters come first in the workspace; the
+  // plan's partial sums follow.
+  const int64_t base = linear_ws_layout(M, K, N).part;
+  if (workspace_bytes < base)
+    return fail(library_scratch ? MX_ERR_UNSUPPORTED : MX_ERR_INVALID_ARGUMENT,
+                "workspace of %lld bytes, at least %lld needed (mx_linear_ws_bytes gives %lld)",
+                (long long)workspace_bytes, (long long)base, (long long)mx_linear_ws_bytes(M, K, N));
+  const uint64_t RN = (uint64_t)mx::slab_rows(N);
+  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2, ybytes = (uint64_t)M * N * 2;
+  auto overlaps_args = [&](uint64_t nbytes) {
+    return !library_scratch &&
+           (overlap(workspace, nbytes, x, xbytes) || overlap(workspace, nbytes, y, ybytes) ||
+            overlap(workspace, nbytes, wq, RN * K) || overlap(workspace, nbytes, ws, RN * (K / 32)) ||
+            overlap(workspace, nbytes, bias, (uint64_t)N * 2));
+  };
+  if (overlaps_args((uint64_t)base)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
+  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, wq, RN * K) || overlap(y, ybytes, ws, RN * (K / 32)) ||
+      overlap(y, ybytes, bias, (uint64_t)N * 2))
+    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if ((st = check_device()) != MX_OK) return st;
+  if (library_scratch) {
+    const hipError_t e = mx::scratch_buffer(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+  }
+  // The plan: the tuned one cached for this shape, else the default rule; a
+  // tuned plan whose partial sums do not fit the workspace gives way to the
+  // default plan.
+  int kind, splits;
+  if ((st = mx_linear_plan_lookup(M, K, N, epilogue, &kind, &splits)) != MX_OK) return st;
+  int64_t need = base + round256(mx_linear_plan_ws_bytes(kind, splits, M, K, N));
+  if (need > workspace_bytes) {
+    if ((st = mx_linear_plan_default(M, K, N, &kind, &splits)) != MX_OK) return st;
+    need = base + round256(mx_linear_plan_ws_bytes(kind, splits, M, K, N));
+  }
+  if (workspace_bytes < need)
+    return fail(library_scratch ? MX_ERR_UNSUPPORTED : MX_ERR_INVALID_ARGUMENT,
+                "workspace of %lld bytes, %lld needed (mx_linear_ws_bytes gives %lld)", (long long)workspace_bytes,
+                (long long)need, (long long)mx_linear_ws_bytes(M, K, N));
+  if (overlaps_args((uint64_t)need)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
+  (void)hipGetLastError();
+  return run_linear_plan(kind, splits, x, M, K, ldx, wq, ws, N, bias, epilogue, y, (uint8_t*)workspace,
+                         (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -838,51 +902,12 @@ int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N) {
 
 int mx_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws, int64_t N,
               const void* bias, int epilogue, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
-  // The token slab lives in the workspace: check it as the operand it becomes.
-  const uint64_t RM0 = M > 0 && M <= kMaxRows ? (uint64_t)mx::slab_rows(M) : 0;
-  const uint8_t* wxq = (const uint8_t*)workspace;
-  const uint8_t* wxs = workspace != nullptr && K > 0 ? wxq + RM0 * (uint64_t)K : nullptr;
-  int st = check_linear_slab(wxq, wxs, M, K, wq, ws, N, bias, epilogue);
-  if (st != MX_OK || M == 0 || N == 0) return st;
-  if (x == nullptr || y == nullptr || workspace == nullptr) return fail(MX_ERR_INVALID_ARGUMENT, "NULL x, y or workspace");
-  if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
-    return fail(MX_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, workspace 256-byte aligned");
-  // The activation slab and the counters come first in the workspace; the
-  // plan's partial sums follow.
-  const int64_t base = linear_ws_layout(M, K, N).part;
-  if (workspace_bytes < base)
-    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, at least %lld needed (mx_linear_ws_bytes gives %lld)",
-                (long long)workspace_bytes, (long long)base, (long long)mx_linear_ws_bytes(M, K, N));
-  const uint64_t RN = (uint64_t)mx::slab_rows(N);
-  const uint64_t xbytes = ((uint64_t)(M - 1) * ldx + K) * 2, ybytes = (uint64_t)M * N * 2;
-  auto overlaps_args = [&](uint64_t nbytes) {
-    return overlap(workspace, nbytes, x, xbytes) || overlap(workspace, nbytes, y, ybytes) ||
-           overlap(workspace, nbytes, wq, RN * K) || overlap(workspace, nbytes, ws, RN * (K / 32)) ||
-           overlap(workspace, nbytes, bias, (uint64_t)N * 2);
-  };
-  if (overlaps_args((uint64_t)base)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
-  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, wq, RN * K) || overlap(y, ybytes, ws, RN * (K / 32)) ||
-      overlap(y, ybytes, bias, (uint64_t)N * 2))
-    return fail(MX_ERR_INVALID_ARGUMENT, "y overlaps an input");
-  if ((st = check_device()) != MX_OK) return st;
-  // The plan: the tuned one cached for this shape, else the default rule; a
-  // tuned plan whose partial sums do not fit the workspace gives way to the
-  // default plan.
-  int kind, splits;
-  if ((st = mx_linear_plan_lookup(M, K, N, epilogue, &kind, &splits)) != MX_OK) return st;
-  int64_t need = base + round256(mx_linear_plan_ws_bytes(kind, splits, M, K, N));
-  if (need > workspace_bytes) {
-    if ((st = mx_linear_plan_default(M, K, N, &kind, &splits)) != MX_OK) return st;
-    need = base + round256(mx_linear_plan_ws_bytes(kind, splits, M, K, N));
-  }
-  if (workspace_bytes < need)
-    return fail(MX_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %lld needed (mx_linear_ws_bytes gives %lld)",
-                (long long)workspace_bytes, (long long)need, (long long)mx_linear_ws_bytes(M, K, N));
-  if (overlaps_args((uint64_t)need)) return fail(MX_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
-  (void)hipGetLastError();
-  return run_linear_plan(kind, splits, x, M, K, ldx, wq, ws, N, bias, epilogue, y, (uint8_t*)workspace,
-                         (hipStream_t)stream);
+  return linear_one_call(x, M, K, ldx, wq, ws, N, bias, epilogue, y, workspace, workspace_bytes, stream, false);
+}
+
+int mx_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws,
+                      int64_t N, const void* bias, int epilogue, void* y, void* stream) {
+  return linear_one_call(x, M, K, ldx, wq, ws, N, bias, epilogue, y, nullptr, mx::kScratchBytes, stream, true);
 }
 
 }  // extern "C"

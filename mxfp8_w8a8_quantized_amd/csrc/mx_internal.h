@@ -99,4 +99,11 @@ hipError_t launch_pc_quantize_slab(int kind, const void* x, int64_t rows, int64_
 hipError_t launch_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
                                  const float* ws, int64_t N, const void* bias, int epi, void* y, hipStream_t stream);
 
+// Bytes of the library-owned scratch array of mx_linear_noalloc (per GPU).
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+
+// Device address of that array on the current device (looked up on the
+// first call per device, then cached).
+hipError_t scratch_buffer(void** ptr);
+
 }  // namespace mx

@@ -393,3 +393,19 @@ def test_probe_rejects_bad_arguments(L):
     assert f(P(A), P(B), 1024, 0, 256, P(D), P(0)) == 1
     assert f(P(A), P(B), 1024, 10, 0, P(D), P(0)) == 1
     assert f(P(A + 2), P(B), 1024, 10, 256, P(D), P(0)) == 1
+
+
+def test_linear_noalloc_rejects_bad_arguments_before_any_launch(L):
+    f = L.mx_linear_noalloc
+
+    def call(x=A, M=8, K=64, ldx=64, wq=B, ws=C, N=256, epi=0, y=D):
+        return f(P(x), M, K, ldx, P(wq), P(ws), N, P(0), epi, P(y), P(0))
+
+    assert call(K=96, ldx=96) == 1  # K % 64
+    assert call(x=0) == 1 and call(y=0) == 1 and call(wq=0) == 1
+    assert call(ldx=60) == 1
+    assert call(y=B) == 1  # y overlaps the weights
+    assert call(N=264) == 2
+    assert call(M=20000, K=5120, ldx=5120) == 2  # activation slab past the 64 MiB scratch array
+    assert b"scratch" in L.mx_last_error_message() or b"needed" in L.mx_last_error_message()
+    assert call(M=0) == 0 and call(N=0) == 0
