@@ -313,10 +313,10 @@ void mx_linear_plan_clear(void);
  * ------------------------------------------------------------------------ */
 
 /* Bytes of workspace mx_linear needs for an M x K x N linear: the activation
- * slab (mx_slab_rows(M) * K * 33 / 32), the few-token kernel's tile counters
- * and the partial sums of any plan mx_linear_tune may pick for the shape,
- * each rounded up to 256 bytes. 0 for M = 0 or N = 0; -1 on a bad shape (K
- * not a positive multiple of 64, sizes past the limits). */
+ * slab (mx_slab_rows(M) * K * 33 / 32) and the partial sums of any plan
+ * mx_linear_tune may pick for the shape, each rounded up to 256 bytes. 0 for
+ * M = 0 or N = 0; -1 on a bad shape (K not a positive multiple of 64, sizes
+ * past the limits). */
 int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N);
 
 /* x bf16 [M][ldx] (ldx >= K, ldx % 8 == 0) is quantized into `workspace`
@@ -325,11 +325,10 @@ int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N);
  * mx_slab_pack) with bias (f16 [N] or NULL) and epilogue into y bf16 [M][N],
  * through the shape's plan (mx_linear_plan_lookup: tuned if mx_linear_tune
  * ran for it, else the default rule; a tuned plan that needs more workspace
- * than given gives way to the default one). The few-token plan with several
- * K ranges adds its partial sums inside the GEMM kernel (the workgroup
- * finishing a tile last reduces it, in range order), so the call is two
- * kernels on `stream` for the slab and few-token plans, three for split-K
- * and balanced ones. Nothing is allocated. workspace: device memory of
+ * than given gives way to the default one): two kernels on `stream` (the
+ * quantizer, then the GEMM), plus the ordered reduction of the partial sums
+ * for plans with several K ranges. Nothing is allocated. workspace: device
+ * memory of
  * mx_linear_ws_bytes(M, K, N) bytes (at least what the chosen plan needs),
  * 256-byte aligned, not overlapping x, the weights, bias or y; its contents
  * are overwritten and need no initial value. K % 64 == 0, N % 16 == 0.
@@ -347,15 +346,15 @@ int mx_linear(const void* x, int64_t M, int64_t K, int64_t ldx,
  * mx_linear, with no workspace argument: its workspace is a scratch array
  * the library owns, 64 MiB of static device memory per GPU, held until the
  * process ends; its device address is looked up once per device, on the
- * first call. Limit: the activation slab, the tile counters and the plan's
- * partial sums must fit in those 64 MiB (a tuned plan that does not fit gives
- * way to the default plan first); larger shapes are MX_ERR_UNSUPPORTED
- * (checked before anything is launched; e.g. up to about 12000 tokens at
- * K = 5120). Every call on a GPU shares that GPU's array and leaves its
- * contents behind (what must start at zero, the kernels clear themselves):
- * calls that overlap in time on one GPU (several streams, concurrent graph
- * replays) race and give wrong results, so serialise them. Nothing is
- * allocated. Other errors: as mx_linear. */
+ * first call. Limit: the activation slab and the plan's partial sums must
+ * fit in those 64 MiB (a tuned plan that does not fit gives way to the
+ * default plan first); larger shapes are MX_ERR_UNSUPPORTED (checked before
+ * anything is launched; e.g. up to about 12000 tokens at K = 5120). Every
+ * call on a GPU shares that GPU's array and leaves its contents behind (no
+ * kernel relies on them: each call writes what it reads): calls that
+ * overlap in time on one GPU (several streams, concurrent graph replays)
+ * race and give wrong results, so serialise them. Nothing is allocated.
+ * Other errors: as mx_linear. */
 int mx_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx,
                       const uint8_t* wq, const uint8_t* ws, int64_t N,
                       const void* bias, int epilogue, void* y, void* stream);

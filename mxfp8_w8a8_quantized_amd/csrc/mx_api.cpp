@@ -770,47 +770,41 @@ namespace {
 int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace layout of mx_linear: the activation slab (codes, then scales),
-// the few-token kernel's tile counters, the plan's partial sums.
+// then the plan's partial sums.
 struct LinearWs {
-  int64_t act, counters, part;  // byte offsets
+  int64_t act, part;  // byte offsets
 };
 
-LinearWs linear_ws_layout(int64_t M, int64_t K, int64_t N) {
+LinearWs linear_ws_layout(int64_t M, int64_t K) {
   const int64_t RM = mx::slab_rows(M);
   LinearWs L;
   L.act = 0;
-  L.counters = round256(RM * K + RM * (K / 32));
-  L.part = L.counters + round256(mx::small_tiles(M, N) * 4);
+  L.part = round256(RM * K + RM * (K / 32));
   return L;
 }
 
-// One linear on the slab operands in the workspace, by plan; the few-token
-// kernel reduces its K ranges in the kernel (counters cleared by the
-// quantizer). The shape checks of the plan's own entry point run first.
+// One linear on the slab operands in the workspace, by plan. The shape
+// checks of the plan's own entry point run first.
 int run_linear_plan(int kind, int splits, const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq,
                     const uint8_t* ws, int64_t N, const void* bias, int epilogue, void* y, uint8_t* work,
                     hipStream_t stream) {
-  const LinearWs L = linear_ws_layout(M, K, N);
+  const LinearWs L = linear_ws_layout(M, K);
   const int64_t RM = mx::slab_rows(M);
   uint8_t* xq = work + L.act;
   uint8_t* xs = xq + RM * K;
-  uint32_t* counters = (uint32_t*)(work + L.counters);
   float* part = (float*)(work + L.part);
   int st = MX_OK;
   if (kind == MX_PLAN_SMALL) st = check_small_shape(M, K, N, splits);
   if (kind == MX_PLAN_SPLITK) st = check_splitk_shape(M, N, splits);
   if (st != MX_OK) return st;
-  const bool fused_reduce = kind == MX_PLAN_SMALL && splits > 1;
-  hipError_t e = mx::launch_quantize_slab(0, x, M, K, ldx, xq, xs, stream, fused_reduce ? counters : nullptr,
-                                          fused_reduce ? (int)mx::small_tiles(M, N) : 0);
+  hipError_t e = mx::launch_quantize_slab(0, x, M, K, ldx, xq, xs, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   switch (kind) {
     case MX_PLAN_SLAB:
       e = mx::launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epilogue, y, stream);
       break;
     case MX_PLAN_SMALL:
-      e = mx::launch_linear_slab_small(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, part, stream,
-                                       fused_reduce ? counters : nullptr);
+      e = mx::launch_linear_slab_small(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, part, stream);
       break;
     case MX_PLAN_SPLITK:
       e = mx::launch_linear_slab_splitk(xq, xs, M, K, wq, ws, N, bias, epilogue, y, splits, part, stream);
@@ -844,9 +838,9 @@ int linear_one_call(const void* x, int64_t M, int64_t K, int64_t ldx, const uint
   if (ldx < K || ldx % 8 != 0) return fail(MX_ERR_INVALID_ARGUMENT, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
     return fail(MX_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, workspace 256-byte aligned");
-  // The activation slab and the counters come first in the workspace; the
-  // plan's partial sums follow.
-  const int64_t base = linear_ws_layout(M, K, N).part;
+  // The activation slab comes first in the workspace; the plan's partial
+  // sums follow.
+  const int64_t base = linear_ws_layout(M, K).part;
   if (workspace_bytes < base)
     return fail(library_scratch ? MX_ERR_UNSUPPORTED : MX_ERR_INVALID_ARGUMENT,
                 "workspace of %lld bytes, at least %lld needed (mx_linear_ws_bytes gives %lld)",
@@ -897,7 +891,7 @@ int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N) {
   if (M == 0 || N == 0) return 0;
   const int64_t part = mx_linear_tune_ws_bytes(M, K, N);  // the largest any candidate plan needs
   if (part < 0) return -1;
-  return linear_ws_layout(M, K, N).part + round256(part);
+  return linear_ws_layout(M, K).part + round256(part);
 }
 
 int mx_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* wq, const uint8_t* ws, int64_t N,

@@ -17,11 +17,8 @@ inline int64_t slab_rows(int64_t rows) { return (rows + 255) / 256 * 256; }
 
 // The same quantization written in the slab layout (codes [K/64][R][64],
 // scales [K/64][R][2], R = slab_rows(rows); pad rows are zero). K % 64 == 0.
-// clear/nclear: nclear uint32 words the kernel sets to zero as well (the
-// in-kernel reduction's tile counters of the GEMM that follows), or none.
 hipError_t launch_quantize_slab(int kind, const void* x, int64_t rows, int64_t K, int64_t ld,
-                                uint8_t* q, uint8_t* s, hipStream_t stream, uint32_t* clear = nullptr,
-                                int nclear = 0);
+                                uint8_t* q, uint8_t* s, hipStream_t stream);
 
 // Row-major codes [rows][K] and scales [rows][K/32] to the slab layout.
 hipError_t launch_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
@@ -71,12 +68,9 @@ hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, int64_t bytes, 
 // A one-wave kernel that occupies `stream` for about `microseconds` (the
 // tuner queues its timed runs behind it, so that they run back to back).
 hipError_t launch_delay(int microseconds, hipStream_t stream);
-// arrivals: null for the two-kernel form (partials, then the reduction
-// kernel); else one zeroed uint32 per tile (small_tiles) and the reduction
-// happens in the GEMM kernel (splits > 1).
 hipError_t launch_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
                                     const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
-                                    float* part, hipStream_t stream, uint32_t* arrivals = nullptr);
+                                    float* part, hipStream_t stream);
 
 // Balanced slab GEMM: the full rounds of ncu tiles data-parallel, the last,
 // partial round split over K (at most 8 ranges, at least 2 slabs each) with

@@ -12,7 +12,7 @@
 
 namespace {
 
-// Activation slab, few-token tile counters and partial sums of one
+// Activation slab and plan partial sums of one
 // mx_linear_noalloc call (the layout of mx_linear's workspace).
 static __device__ __align__(256) uint8_t scratch[mx::kScratchBytes];
 

@@ -28,10 +28,7 @@ constexpr int64_t kMaxBlocks = 65536;
 
 template <bool F32, bool SLAB, typename Idx>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restrict__ x, Idx rows, Idx K, Idx ld,
-                                                            Idx R, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                            uint32_t* __restrict__ clear, int nclear) {
-  // Words the GEMM that follows needs at zero (its tile counters), if any.
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < nclear; i += gridDim.x * kThreads) clear[i] = 0u;
+                                                            Idx R, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const Idx qpr = K / 8;  // quarters per row; a multiple of 4
   const Idx total = (SLAB ? R : rows) * qpr;
   const Idx stride = (Idx)gridDim.x * kThreads;
@@ -128,17 +125,16 @@ int64_t grid_for(int64_t units, int64_t per_block) {
 }
 
 template <bool F32, bool SLAB>
-hipError_t launch_typed(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s, hipStream_t st,
-                        uint32_t* clear = nullptr, int nclear = 0) {
+hipError_t launch_typed(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s, hipStream_t st) {
   const int64_t R = SLAB ? slab_rows(rows) : rows;
   const int64_t total = R * (K / 8);
   const unsigned blocks = (unsigned)grid_for(total, (int64_t)kThreads * kItems);
   if (total < (int64_t)1 << 31 && rows * ld < (int64_t)1 << 31 && R * K < (int64_t)1 << 31) {
     hipLaunchKernelGGL((quantize_kernel<F32, SLAB, uint32_t>), dim3(blocks), dim3(kThreads), 0, st, x,
-                       (uint32_t)rows, (uint32_t)K, (uint32_t)ld, (uint32_t)R, q, s, clear, nclear);
+                       (uint32_t)rows, (uint32_t)K, (uint32_t)ld, (uint32_t)R, q, s);
   } else {
     hipLaunchKernelGGL((quantize_kernel<F32, SLAB, uint64_t>), dim3(blocks), dim3(kThreads), 0, st, x,
-                       (uint64_t)rows, (uint64_t)K, (uint64_t)ld, (uint64_t)R, q, s, clear, nclear);
+                       (uint64_t)rows, (uint64_t)K, (uint64_t)ld, (uint64_t)R, q, s);
   }
   return hipGetLastError();
 }
@@ -152,9 +148,9 @@ hipError_t launch_quantize(int kind, const void* x, int64_t rows, int64_t K, int
 }
 
 hipError_t launch_quantize_slab(int kind, const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* q, uint8_t* s,
-                                hipStream_t stream, uint32_t* clear, int nclear) {
-  return kind == 1 ? launch_typed<true, true>(x, rows, K, ld, q, s, stream, clear, nclear)
-                   : launch_typed<false, true>(x, rows, K, ld, q, s, stream, clear, nclear);
+                                hipStream_t stream) {
+  return kind == 1 ? launch_typed<true, true>(x, rows, K, ld, q, s, stream)
+                   : launch_typed<false, true>(x, rows, K, ld, q, s, stream);
 }
 
 hipError_t launch_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, uint8_t* qo, uint8_t* so,

@@ -58,7 +58,6 @@ struct SmallParams {
   const uint16_t* bias;
   uint16_t* y;
   float* part;  // [splits][M][N] f32 when splits > 1
-  uint32_t* arrivals;  // in-kernel reduction: one zeroed counter per tile (else null)
   int M, N, K;
   int64_t RM, RN;
   int tiles_m, tiles_n, splits;
@@ -79,19 +78,8 @@ struct Pair {
 // 8 waves, two per SIMD: wave w computes the 32 x 32 block of token rows
 // 32 (w%4) .. and weight rows 32 (w/4) ..; while one wave of a SIMD waits
 // (for its MFMA to issue, at the barrier, for LDS data) the other issues.
-// FUSE (with PART): the reduction happens in this kernel. Each workgroup
-// writes its range's partial sums, waits for its own stores, and counts
-// itself in on the tile's counter after a device-scope release (the L2
-// written back, so the partials are visible to the other XCDs); the
-// workgroup that arrives last acquires (invalidating stale cached lines),
-// adds the ranges' partials in range order exactly as small_reduce_kernel
-// does, and writes bias + epilogue + bf16. Nobody waits for anybody: the
-// counters only decide which workgroup finishes the tile. They must be zero
-// when the kernel starts (the activation quantizer of the one-call path
-// clears them).
-template <int EPI, bool PART, int RP, bool FUSE = false>
+template <int EPI, bool PART, int RP>
 __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
-  static_assert(PART || !FUSE, "the in-kernel reduction reduces partials");
   static_assert(RP % 3 == 0 && RP >= 3, "the ring unrolls with three fragment sets");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -207,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
   // They are older than every slab load, so the slab waits below (loads
   // complete in order) cover them too.
   i32x2 bq[4];
-  if constexpr (!PART || FUSE) {
+  if constexpr (!PART) {
     const bool has_b = p.bias != nullptr;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(has_b ? p.bias + n0 : nullptr, has_b ? (uint32_t)(p.N - n0) * 2u : 0u);
 #pragma unroll
@@ -243,42 +231,7 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
         *(f32x4*)(prow + n) = v;
       }
     }
-  }
-  if constexpr (FUSE) {
-    __shared__ int last;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials are in the L2
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __threadfence();  // release: write the L2 back for the other XCDs
-      const uint32_t before = __hip_atomic_fetch_add(p.arrivals + (tn * p.tiles_m + tm), 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-      last = before == (uint32_t)(p.splits - 1);
-      if (last) __threadfence();  // acquire: drop stale cached copies of the other ranges' partials
-    }
-    __syncthreads();
-    if (!last) return;
-    const size_t plane = (size_t)p.M * p.N;
-    const float* src = p.part + (size_t)(m_ok ? m : 0) * p.N;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 32 * wf + 8 * q + 4 * hi;
-      if (m_ok && n < p.N) {
-        f32x4 t = *(const f32x4*)(src + n);
-        for (int k = 1; k < p.splits; ++k) {
-          const f32x4 v = *(const f32x4*)(src + k * plane + n);
-          t[0] += v[0];
-          t[1] += v[1];
-          t[2] += v[2];
-          t[3] += v[3];
-        }
-        acc[4 * q] = t[0];
-        acc[4 * q + 1] = t[1];
-        acc[4 * q + 2] = t[2];
-        acc[4 * q + 3] = t[3];
-      }
-    }
-  }
-  if constexpr (!PART || FUSE) {
+  } else {
     const int rows = min(p.M - m0, TM);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + (size_t)m0 * p.N, (uint32_t)rows * (uint32_t)p.N * 2u);
 #pragma unroll
@@ -333,10 +286,10 @@ __global__ __launch_bounds__(256) void small_reduce_kernel(SmallParams p) {
   *(i32x2*)(p.y + (size_t)m * p.N + n) = i32x2{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1)};
 }
 
-template <int EPI, bool PART, bool FUSE = false>
+template <int EPI, bool PART>
 hipError_t launch_small_kernel(const SmallParams& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
-  auto kern = small_kernel<EPI, PART, kSteps, FUSE>;
+  auto kern = small_kernel<EPI, PART, kSteps>;
   constexpr int lds = kSteps * PAIR;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -370,9 +323,8 @@ int64_t small_tiles(int64_t M, int64_t N) { return ((M + TM - 1) / TM) * ((N + T
 
 hipError_t launch_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
                                     const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
-                                    float* part, hipStream_t stream, uint32_t* arrivals) {
+                                    float* part, hipStream_t stream) {
   SmallParams p;
-  p.arrivals = arrivals;
   p.x = xq;
   p.xs = xs;
   p.wq = wq;
@@ -391,9 +343,6 @@ hipError_t launch_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_
   const int nwg = p.tiles_m * p.tiles_n * p.splits;
   if (p.splits == 1)
     return epi == 1 ? launch_small_kernel<1, false>(p, nwg, stream) : launch_small_kernel<0, false>(p, nwg, stream);
-  if (arrivals != nullptr)
-    return epi == 1 ? launch_small_kernel<1, true, true>(p, nwg, stream)
-                    : launch_small_kernel<0, true, true>(p, nwg, stream);
   hipError_t e = launch_small_kernel<0, true>(p, nwg, stream);
   if (e != hipSuccess) return e;
   const unsigned nred = (unsigned)((M * (N / 4) + 255) / 256);

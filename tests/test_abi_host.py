@@ -155,18 +155,17 @@ def test_slab_calls_reject_bad_arguments(L):
 
 
 def test_linear_one_call_sizes_and_bad_arguments(L):
-    # activation slab, then 4 bytes per few-token tile, then the largest
-    # partial-sum workspace of the tuner's candidates; each rounded to 256
+    # activation slab, then the largest partial-sum workspace of the tuner's
+    # candidates; each rounded to 256
     r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
     act = r256(512 * 5120 + 512 * 160)
-    counters = r256(3 * 80 * 4)  # 300 tokens, 5120 weight rows: 3 x 80 tiles of 128 x 64
-    assert L.mx_linear_ws_bytes(300, 5120, 5120) == act + counters + r256(L.mx_linear_tune_ws_bytes(300, 5120, 5120))
+    assert L.mx_linear_ws_bytes(300, 5120, 5120) == act + r256(L.mx_linear_tune_ws_bytes(300, 5120, 5120))
     assert L.mx_linear_tune_ws_bytes(300, 5120, 5120) == 8 * 2 * 20 * 65536 * 4  # split-K 8: the largest
     assert L.mx_linear_ws_bytes(0, 64, 16) == 0 and L.mx_linear_ws_bytes(4, 64, 0) == 0
     assert L.mx_linear_ws_bytes(1, 96, 16) == -1 and L.mx_linear_ws_bytes(-1, 64, 16) == -1
     f = L.mx_linear
     need = L.mx_linear_ws_bytes(8, 64, 256)
-    assert need == r256(256 * 64 + 256 * 2) + 256  # one K slab: only unsplit plans, no partial sums
+    assert need == r256(256 * 64 + 256 * 2)  # one K slab: only unsplit plans, no partial sums
     E = 0x50000000
 
     def call(x=A, M=8, K=64, ldx=64, wq=B, ws=C, N=256, epi=0, y=D, wsp=E, nb=need):

@@ -1,14 +1,10 @@
 """The one-call linear (mx_linear): quantizer into the caller's workspace,
-then the GEMM through the shape's plan, with the few-token kernel adding its
-K ranges' partial sums inside the GEMM kernel (the workgroup that finishes a
-tile last reduces it).
+then the GEMM through the shape's plan (tuned, else the default rule).
 
 Each case: the output equals the two-call path with the same plan
-(mx_quantize_act_slab + mx_linear_slab_planned, whose few-token reduction is a
-separate kernel summing the ranges in the same order) bit for bit, and the
-oracle within 1e-3 g sum|a||b| + one bf16 ulp on every element. The
-workspace needs no initial value (the quantizer clears the tile counters),
-so it is filled with 0xFF first and the call is repeated.
+(mx_quantize_act_slab + mx_linear_slab_planned) bit for bit, and the oracle
+within 1e-3 g sum|a||b| + one bf16 ulp on every element. The workspace needs
+no initial value, so it is filled with 0xFF first and the call is repeated.
 
 Source of the rule: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound
 OptRTN)", section "Quantization Details".
@@ -96,7 +92,7 @@ def test_one_call_takes_the_tuned_plan():
     mx().mx_linear_plan_clear()
 
 
-def test_one_call_nonfinite_through_in_kernel_reduction():
+def test_one_call_nonfinite_few_token_ranges():
     """NaN / Inf groups on the few-token plan with K ranges: NaN rows and
     columns exactly where the oracle has them."""
     M, K, N = 100, 640, 272
@@ -116,10 +112,9 @@ def test_one_call_nonfinite_through_in_kernel_reduction():
 
 
 def test_one_call_graph_replays_match_eager():
-    """The one-call linear on the few-token plan captured in a HIP graph:
-    the quantizer's counter clearing is a kernel, so every replay starts
-    from zeroed counters; replays with eager work between them equal the
-    eager call bit for bit."""
+    """The one-call linear on the few-token plan (quantizer, GEMM over K
+    ranges, ordered reduction) captured in a HIP graph: replays with eager
+    work between them equal the eager call bit for bit."""
     M, K, N = 128, 1024, 1024
     d = dev()
     inputs = [synth.make_activation(M, K, seed=s).to(d) for s in (81, 82, 83)]
