@@ -33,11 +33,13 @@ Prints ONE JSON line. Besides the contract fields it carries
                 (40 blocks) back to back, and one GPU's share of a two-way
                 tensor-parallel split of four linears.
 
-Modes for profiling: --profile step|rowmajor|fused runs only those kernels
-(steps times, no oracle); --profile workloads runs the other workloads (FFN
-pair, cross-attention set, 128-token linear, per-channel FP8 step, one whole
-denoise step) twice each; --profile-copy runs a 1 GiB device copy used to
-calibrate the HBM byte counters.
+Modes for profiling: --profile step|quant|rowmajor|fused runs only those kernels
+(steps times, no oracle); --profile single|ffn|xattn runs one of the other
+workloads (the 128-token linear; the FFN pair as two one-call linears, then
+with the requantizing epilogue; the cross-attention set); --profile workloads
+runs all of them, the per-channel FP8 step and one whole denoise step twice
+each; --profile-copy runs a 1 GiB device copy (its GB/s, and the calibration
+of the HBM byte counters).
 """
 
 import argparse
@@ -89,7 +91,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--profile", choices=["step", "rowmajor", "fused", "workloads"], help="run only these kernels")
+    ap.add_argument("--profile", choices=["step", "rowmajor", "fused", "workloads", "quant", "single", "ffn", "xattn"],
+                    help="run only these kernels")
     ap.add_argument("--profile-copy", action="store_true", help="run only a 1 GiB device copy")
     return ap.parse_args()
 
@@ -350,6 +353,48 @@ def other_workloads(torch, mx, synth, dev, steps=10, warmup=3):
     return res
 
 
+def profile_config(torch, mx, synth, dev, which, steps, warmup):
+    """Runs one of the other workloads' linears alone (for kernel traces and
+    counters): "single" the 128-token linear, "ffn" the FFN pair as two
+    one-call linears and then with the requantizing epilogue, "xattn" the
+    cross-attention set; each through mx_linear with the default plans."""
+    name = {"single": "single_128x5120x5120", "ffn": "ffn_75348x5120x13824", "xattn": "xattn_512x5120x10240"}[which]
+    layers = []
+    for li, shp in enumerate(synth.CONFIGS[name]):
+        w = mx.mx_quantize_weight_slab(synth.make_weight_device(shp.N, shp.K, 500 + li, dev))
+        b = synth.make_bias(shp.N, 500 + li).to(dev)
+        if shp.name == "ffn.net.2":
+            x = None
+        elif shp.M == synth.TEXT_TOKENS:
+            x = synth.make_text_context(shp.M, shp.K, 500 + li).to(dev)
+        else:
+            x = synth.make_activation_device(shp.M, shp.K, 500 + li, dev)
+        y = torch.empty((shp.M, shp.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((max(mx.mx_linear_ws_bytes(shp.M, shp.K, shp.N), 1),), dtype=torch.uint8, device=dev)
+        layers.append((shp, w, b, x, y, ws))
+
+    def run():
+        for li, (shp, w, b, x, y, ws) in enumerate(layers):
+            mx.mx_linear(x if x is not None else layers[li - 1][4], w, b, gelu=shp.gelu, y=y, workspace=ws)
+
+    fns = [run]
+    if which == "ffn":
+        (s1, w1, b1, x1, _, ws1), (s2, w2, b2, _, y2, _) = layers
+        xs = mx.mx_quantize_act_slab(x1)
+        h = mx.mx_linear_slab_requant(xs, w1, b1, gelu=True)
+
+        def run_requant():
+            mx.mx_quantize_act_slab(x1, xs)
+            mx.mx_linear_slab_requant(xs, w1, b1, gelu=True, out=h)
+            mx.mx_linear_slab(h, w2, b2, y=y2)
+
+        fns.append(run_requant)
+    timed_step(torch, fns, steps, warmup)
+    print(json.dumps({"profiled": which, "steps": steps,
+                      "linears": [f"{shp.name} {shp.M}x{shp.K}x{shp.N} {mx.plan_lookup(shp.M, shp.K, shp.N, shp.gelu)}"
+                                  for shp, *_ in layers]}), flush=True)
+
+
 def denoise_step(torch, synth, dev, steps=2, warmup=1):
     """One full denoise step's quantized linears, back to back: 40 blocks x
     10 linears (q|k|v and the text k|v fused, 7 GEMMs a block), each with its
@@ -467,10 +512,10 @@ def main():
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        b.copy_(a)
+        total, _ = timed_step(torch, [lambda: b.copy_(a)], 3, 1)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5,
+                          "copy_GBps": round(2 * n / (total / 3 * 1e-3) / 1e9, 1)}))
         return
 
     if not os.path.exists(mx.LIB_PATH):
@@ -479,6 +524,9 @@ def main():
         __graft_entry__.build()
 
     shape = synth.CONFIGS[WORKLOAD][0]
+    if args.profile in ("single", "ffn", "xattn"):
+        profile_config(torch, mx, synth, dev, args.profile, args.steps, args.warmup)
+        return
     if args.profile == "workloads":
         res = {
             "other_workloads": other_workloads(torch, mx, synth, dev, steps=2, warmup=1),
@@ -514,7 +562,8 @@ def main():
     del w
 
     if args.profile:
-        fns = {"step": [quant, gemm], "rowmajor": rowmajor, "fused": [fused] if rowmajor else None}[args.profile]
+        fns = {"step": [quant, gemm], "quant": [quant], "rowmajor": rowmajor,
+               "fused": [fused] if rowmajor else None}[args.profile]
         timed_step(torch, fns, args.steps, args.warmup)
         print(json.dumps({"profiled": args.profile, "steps": args.steps}), flush=True)
         return

@@ -34,7 +34,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restri
   const Idx stride = (Idx)gridDim.x * kThreads;
   const Idx gpr = K / 32;
   const Idx nslab = K / 64;
-  for (Idx base = (Idx)blockIdx.x * kThreads + threadIdx.x; base < total; base += stride * kItems) {
+  // Slab order: the 32 row pairs whose scales share one 128-byte line of a
+  // scale slab are 5 blocks apart (at K = 5120). Blocks are dealt to the 8
+  // XCDs in turn, so give each XCD a contiguous range of logical blocks:
+  // the pieces of a scale line are then written by blocks on one XCD, at
+  // about the same time, and its L2 merges them into whole lines (dealt
+  // round-robin, the line's pieces reached several L2s, each of which wrote
+  // back a partial line).
+  Idx lb = blockIdx.x;
+  if (SLAB) {
+    const Idx nb = gridDim.x, q8 = nb >> 3, r8 = nb & 7, xcd = blockIdx.x & 7;
+    lb = xcd * q8 + (xcd < r8 ? xcd : r8) + (blockIdx.x >> 3);
+  }
+  for (Idx base = lb * kThreads + threadIdx.x; base < total; base += stride * kItems) {
     // All four lanes of a quad see the same validity and row: total and
     // stride are multiples of 4 (of 16 in slab order) and quads are 4-aligned.
     uint32_t raw[kItems][8];
