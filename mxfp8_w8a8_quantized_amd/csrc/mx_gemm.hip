@@ -287,12 +287,24 @@ __global__ __launch_bounds__(NT, 1) void linear_kernel(Params p) {
 
   const int wave = threadIdx.x >> 6;
   const int wn = wave >> 1, wm = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, r16 = lane & 15;
 
+  // Accumulators start at the bias (bias + K sum in fp32, as every GEMM
+  // kernel here computes it); lane holds n = 16 i + 4 G + r of its wave tile.
   f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int nl = wn * 128 + 16 * i + 4 * G;
+    f32x4 b = {0.f, 0.f, 0.f, 0.f};
+    if (p.bias != nullptr && nl < rows_n) {
+      const uint16_t* bp = p.bias + n0 + nl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, bp[r]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = b;
+  }
 
   Fp8Regs wr;
   Fp8Regs xr8;
@@ -327,26 +339,18 @@ __global__ __launch_bounds__(NT, 1) void linear_kernel(Params p) {
   }
 
   // Epilogue: lane holds D[n = 16 i + 4 G + r][m = 16 j + l%16] of its wave tile.
-  const int lane = threadIdx.x & 63;
-  const int G = lane >> 4, r16 = lane & 15;
   const int N = p.N;
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + (size_t)m0 * N, (uint32_t)(rows_m * N * 2));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int nl = wn * 128 + 16 * i + 4 * G;  // local n of element r = 0
     const bool n_ok = nl < rows_n;
-    float b[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.bias != nullptr && n_ok) {
-      const uint16_t* bp = p.bias + n0 + nl;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = (float)__builtin_bit_cast(_Float16, bp[r]);
-    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ml = wm * 128 + 16 * j + r16;
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][r] + b[r]);
+      for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][r]);
       const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
       const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
       const i32x2 out = {__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1)};
@@ -472,7 +476,7 @@ __device__ __forceinline__ void mma8(f32x16 (&acc)[4][2], const Frags& F) {
 // PC (per-channel FP8): each accumulator is first multiplied by its token
 // row's and weight row's f32 scales, read from the LDS table `tab`
 // ([0, 256) weight rows of the tile, [256, 512) token rows).
-template <int EPI, int MF = 2, bool PC = false>
+template <int EPI, int MF = 2, bool PC = false, bool BIAS_IN_ACC = false>
 __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const BiasQuads& B, const Params& p,
                                             uint8_t* ep, int m0, int n0, int rows_m, int rows_n, int wn, int wm,
                                             int lane, const float* tab = nullptr) {
@@ -484,7 +488,7 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Bi
       const int nb = 8 * i + 2 * q + hi;
       float b[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = bias_at(B, 4 * i + q, r);
+      for (int r = 0; r < 4; ++r) b[r] = BIAS_IN_ACC ? 0.f : bias_at(B, 4 * i + q, r);
       f32x4 swq = {1.f, 1.f, 1.f, 1.f};
       if constexpr (PC) swq = *(const f32x4*)(tab + wn * 128 + 4 * nb);
 #pragma unroll
@@ -495,6 +499,9 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Bi
           const float sxm = tab[256 + wm * 32 * MF + m];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] * (sxm * swq[r]) + b[r]);
+        } else if constexpr (BIAS_IN_ACC) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r]);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] + b[r]);
@@ -556,13 +563,24 @@ __global__ __launch_bounds__(NT8, 1) void linear_prequant_pp(Params p) {
   S.voff1 = (lane >> 3) * K + (((lane & 7) ^ ((4 + (lane >> 4)) & 7)) << 4);
   S.soff = lane * G32;
 
+  // Accumulators start at the bias (an output is bias + its K sum in fp32,
+  // the order of the slab kernel, so the two layouts give identical bits).
+  BiasQuads B;
+  load_bias_quads(B, p, n0, rows_n, wn, lane);
+  if (loader) issue_stage(S, smem, 0, true, wave);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float b = bias_at(B, 4 * i + q, r);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j][4 * q + r] = b;
+      }
 
-  if (loader) issue_stage(S, smem, 0, true, wave);
   for (int k = 0; k < nk; ++k) {
     uint8_t* cur = smem + (k & 1) * STAGE;
     uint8_t* nxt = smem + ((k + 1) & 1) * STAGE;
@@ -581,11 +599,9 @@ __global__ __launch_bounds__(NT8, 1) void linear_prequant_pp(Params p) {
     mma8(acc, F1);
   }
   __builtin_amdgcn_sched_barrier(0);
-  BiasQuads B;
-  load_bias_quads(B, p, n0, rows_n, wn, lane);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  store_tile8<EPI>(acc, B, p, smem + wave * 16384, m0, n0, rows_m, rows_n, wn, wm, lane);
+  store_tile8<EPI, 2, false, true>(acc, B, p, smem + wave * 16384, m0, n0, rows_m, rows_n, wn, wm, lane);
 }
 
 template <int EPI>
@@ -876,7 +892,7 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
 // K'-slabs; 4 rows per read make whole 256-byte runs in each slab. Rows past
 // M are written as zero codes and scales (the slab's pad rows); columns past
 // N are dropped.
-template <int EPI>
+template <int EPI, bool BIAS_IN_ACC>
 __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const BiasQuads& B, const Params& p,
                                              uint8_t* ep, int m0, int n0, int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
@@ -887,13 +903,13 @@ __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Bi
       const int nb = 8 * i + 2 * q + hi;
       float b[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = bias_at(B, 4 * i + q, r);
+      for (int r = 0; r < 4; ++r) b[r] = BIAS_IN_ACC ? 0.f : bias_at(B, 4 * i + q, r);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = 32 * j + r32;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] + b[r]);
+        for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(BIAS_IN_ACC ? acc[i][j][4 * q + r] : acc[i][j][4 * q + r] + b[r]);
         const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
         const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
         *(i32x2*)(ep + m * 256 + ((nb ^ ((m & 15) << 1)) << 3)) =
@@ -964,6 +980,42 @@ __device__ __forceinline__ void store_tile_part(const f32x16 (&acc)[4][4], const
 enum { OUT_Y = 0, OUT_Q = 1, OUT_PART = 2, OUT_PCY = 3 };
 constexpr int PC_TABLE = LDS;  // byte offset of the per-channel scale table
 constexpr int LDS_PC = LDS + 2048;
+// Bias: each wave copies the 128 f16 bias values of its weight-row half (wn)
+// into its own 256-byte LDS slot past the ring and the per-channel table,
+// with one 4-byte DMA per lane issued before the ring's first stages; waiting
+// for that one load (the oldest) leaves the ring's loads in flight. The bf16
+// and requantizing outputs then start their accumulators at the bias (an
+// output is bias + its K sum, in fp32), which takes the bias adds out of the
+// epilogue and puts the accumulator initialization inside the first stage's
+// load latency; the per-channel output, whose bias follows the row scales,
+// reads its slot in the epilogue. Before: the epilogue waited a memory round
+// trip for the bias after the last MFMA (0.85 us of a 61 us tile at
+// 75348 x 5120 x 15360). Without a bias the slot is zeroed with ordinary LDS
+// writes. Columns past N (a ragged last weight tile) read whatever the DMA
+// leaves there; their outputs are not stored.
+constexpr int BIAS_TABLE = LDS_PC;
+constexpr int LDS_OUT = LDS_PC + 4 * 256;
+
+template <int OUT>
+constexpr int lds_bytes() { return OUT == OUT_PART ? LDS : LDS_OUT; }
+
+__device__ __forceinline__ void issue_bias_slot(const Params& p, uint8_t* smem, int n0, int rows_n, int wave, int wn,
+                                                int lane) {
+  uint8_t* slot = smem + BIAS_TABLE + wave * 256;
+  if (p.bias != nullptr) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias + n0, (uint32_t)rows_n * 2u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)slot, 4, lane * 4, wn * 256, 0, 0);
+  } else {
+    *(int*)(slot + lane * 4) = 0;
+  }
+}
+
+// The wave's bias quads from its slot, in the layout load_bias_quads gives.
+__device__ __forceinline__ void read_bias_quads(BiasQuads& B, const uint8_t* smem, int wave, int lane) {
+  const uint8_t* base = smem + BIAS_TABLE + wave * 256 + 4 * (lane >> 5) * 2;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) B.v[k] = *(const i32x2*)(base + (32 * (k >> 2) + 8 * (k & 3)) * 2);
+}
 
 template <int EPI, int OUT>
 __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
@@ -1006,11 +1058,35 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  constexpr bool BIAS_IN_ACC = OUT == OUT_Y || OUT == OUT_Q;
+  if constexpr (OUT != OUT_PART) issue_bias_slot(p, smem, n0, rows_n, wave, wn, lane);
   issue_half<PC>(S, smem, 0, wave, lane);
   issue_half<PC>(S, smem, 1, wave, lane);
   issue_half<PC>(S, smem, 2, wave, lane);
   issue_half<PC>(S, smem, 3, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (BIAS_IN_ACC) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(4 * loads_per_half<PC>()) : "memory");
+    BiasQuads B0;
+    read_bias_quads(B0, smem, wave, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float b = bias_at(B0, 4 * i + q, r);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[i][jj][4 * q + r] = b;
+        }
+    // Materialize the accumulators here, inside the first stage's latency
+    // (left alone, the compiler moves their writes past the barrier below).
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) asm volatile("" : "+a"(acc[i][jj]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * loads_per_half<PC>()) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -1025,7 +1101,7 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   if (j < nh) half_step<PC>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
   __builtin_amdgcn_sched_barrier(0);
   BiasQuads B;
-  if constexpr (OUT != OUT_PART) load_bias_quads(B, p, n0, rows_n, wn, lane);
+  if constexpr (OUT == OUT_PCY) read_bias_quads(B, smem, wave, lane);
   float scw = 0.f, scx = 0.f;
   if constexpr (PC) {
     // One weight-row and one token-row scale per thread; zero past N and M.
@@ -1043,12 +1119,12 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   }
   __builtin_amdgcn_s_barrier();
   if constexpr (OUT == OUT_Q)
-    store_tile_q<EPI>(acc, B, p, smem + wave * 32768, m0, n0, wn, wm, lane);
+    store_tile_q<EPI, true>(acc, B, p, smem + wave * 32768, m0, n0, wn, wm, lane);
   else if constexpr (OUT == OUT_PART)
     store_tile_part(acc, p, bid, ks, m0, wave, wm, lane);
   else
-    pp::store_tile8<EPI, 4, PC>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane,
-                                (const float*)(smem + PC_TABLE));
+    pp::store_tile8<EPI, 4, PC, BIAS_IN_ACC>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane,
+                                             (const float*)(smem + PC_TABLE));
 }
 
 // Split-K reduction: one thread per 16-byte chunk of the partial tiles (the
@@ -1094,7 +1170,7 @@ template <int EPI, int OUT = OUT_Y>
 hipError_t launch(const Params& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
   auto kern = linear_slab_kernel<EPI, OUT>;
-  constexpr int lds = OUT == OUT_PCY ? LDS_PC : LDS;
+  constexpr int lds = lds_bytes<OUT>();
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
