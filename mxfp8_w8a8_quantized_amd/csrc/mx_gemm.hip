@@ -883,36 +883,37 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
 
 // Requantizing epilogue: instead of y, the MX quantization of y (bf16) in
 // the slab layout, as the next linear takes it (K' = N; the FFN
-// down-projection after the GELU up-projection). The wave's 128 x 128 bf16
-// results are staged in LDS as in the plain epilogue (8-byte block nb of row
-// m at nb ^ ((m & 15) << 1), so that two neighbouring blocks stay adjacent);
-// then each lane reads 8 consecutive values of a row, the 4 lanes of a DPP
-// quad hold one group of 32, and quantize8_bf16 encodes them exactly as the
-// quantizer does. 16 lanes cover a row's 128 values, i.e. two 64-wide
+// down-projection after the GELU up-projection). The accumulators already
+// hold the bias. The wave's 128 x 128 bf16 results are staged in LDS as in
+// the plain epilogue (8-byte block nb of row m at nb ^ (m & 31): 32 lanes on
+// 32 consecutive rows write 32 distinct bank pairs; the earlier swizzle
+// nb ^ ((m & 15) << 1) kept block pairs adjacent but was 2-way bank
+// conflicted, 16 M conflict cycles per launch at 75348 x 5120 x 13824); then
+// each lane reads 8 consecutive values of a row (one aligned 16-byte pair,
+// its halves swapped back when the row's swizzle is odd), the 4 lanes of a
+// DPP quad hold one group of 32, and quantize8_bf16 encodes them exactly as
+// the quantizer does. 16 lanes cover a row's 128 values, i.e. two 64-wide
 // K'-slabs; 4 rows per read make whole 256-byte runs in each slab. Rows past
 // M are written as zero codes and scales (the slab's pad rows); columns past
 // N are dropped.
-template <int EPI, bool BIAS_IN_ACC>
-__device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const BiasQuads& B, const Params& p,
-                                             uint8_t* ep, int m0, int n0, int wn, int wm, int lane) {
+template <int EPI>
+__device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Params& p, uint8_t* ep, int m0, int n0,
+                                             int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nb = 8 * i + 2 * q + hi;
-      float b[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = BIAS_IN_ACC ? 0.f : bias_at(B, 4 * i + q, r);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = 32 * j + r32;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(BIAS_IN_ACC ? acc[i][j][4 * q + r] : acc[i][j][4 * q + r] + b[r]);
+        for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r]);
         const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
         const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
-        *(i32x2*)(ep + m * 256 + ((nb ^ ((m & 15) << 1)) << 3)) =
+        *(i32x2*)(ep + m * 256 + ((nb ^ (m & 31)) << 3)) =
             i32x2{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1)};
       }
     }
@@ -930,7 +931,9 @@ __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Bi
   for (int it = 0; it < 32; ++it) {
     const int row = 4 * it + (lane >> 4);
     const int mg = m0 + wm * 128 + row;
-    i32x4 v = *(const i32x4*)(ep + row * 256 + (((2 * c) ^ ((row & 15) << 1)) << 3));
+    const int sw = row & 31;
+    i32x4 v = *(const i32x4*)(ep + row * 256 + ((((2 * c) ^ sw) & ~1) << 3));
+    if (sw & 1) v = i32x4{v[2], v[3], v[0], v[1]};
     if (mg >= p.M) v = i32x4{0, 0, 0, 0};
     const uint32_t raw[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
     uint32_t codes[2], sc;
@@ -1119,7 +1122,7 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   }
   __builtin_amdgcn_s_barrier();
   if constexpr (OUT == OUT_Q)
-    store_tile_q<EPI, true>(acc, B, p, smem + wave * 32768, m0, n0, wn, wm, lane);
+    store_tile_q<EPI>(acc, p, smem + wave * 32768, m0, n0, wn, wm, lane);
   else if constexpr (OUT == OUT_PART)
     store_tile_part(acc, p, bid, ks, m0, wave, wm, lane);
   else
