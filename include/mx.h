@@ -104,9 +104,10 @@ int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t 
  * the dequantized weights (wq, ws). Products are exact, sums are FP32.
  * x: bf16 [M][K]; wq: uint8 [N][K]; ws: uint8 [N][K/32]; bias: f16 [N] or
  * NULL; epilogue: mx_epilogue; y: bf16 [M][N]. Correct for any K % 32 == 0
- * but slow: its kernel holds the bf16 token tile beside 256 accumulators per
- * lane and spills (about 240 TFLOP/s at 75348 x 5120 x 15360, against about
- * 2700 for mx_linear). Kept for callers without slab weights or workspace. */
+ * but slow: every 256 x 256 tile quantizes its bf16 token rows again, and the
+ * kernel holds them beside 256 accumulators per lane and spills (about 760
+ * TFLOP/s at 75348 x 5120 x 15360, against about 2600 for mx_linear). Kept
+ * for callers without slab weights or workspace. */
 int mx_linear_fused(const void* x, int64_t M, int64_t K,
                     const uint8_t* wq, const uint8_t* ws, int64_t N,
                     const void* bias, int epilogue, void* y, void* stream);
