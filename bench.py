@@ -122,6 +122,20 @@ def timed_step(torch, fns, steps, warmup):
     return start.elapsed_time(end), per
 
 
+def device_copy_gbps(torch, dev, steps=10, warmup=3):
+    """GB/s of a plain 1 GiB device-to-device copy (torch's copy kernel):
+    read + write bytes over time, the practical HBM rate that an HBM-bound
+    kernel moving about as much as it reads can be held to on this GPU."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    total, _ = timed_step(torch, [lambda: b.copy_(a)], steps, warmup)
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * n / (total / steps * 1e-3) / 1e9, 1)
+
+
 def graph_ms(torch, fn, reps, per_graph=5):
     """ms per call of fn replayed from a captured HIP graph (per_graph calls
     per graph), i.e. without the host's launch cost: what a serving loop
@@ -513,12 +527,8 @@ def main():
 
     if args.profile_copy:
         n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        total, _ = timed_step(torch, [lambda: b.copy_(a)], 3, 1)
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5,
-                          "copy_GBps": round(2 * n / (total / 3 * 1e-3) / 1e9, 1)}))
+                          "copy_GBps": device_copy_gbps(torch, dev, 3, 1)}))
         return
 
     if not os.path.exists(mx.LIB_PATH):
@@ -637,10 +647,13 @@ def main():
         _, (f_ms,) = timed_step(torch, [fused], 10, 2)
         fa = mean(f_ms)
         cold = cold_steps(torch, dev, [quant, gemm], 10)
+        copy_gbps = device_copy_gbps(torch, dev)
         out["extra"] = {
             "quantize_act_ms": round(qa, 4),
             "quantize_act_GBps": round(act_bytes / (qa * 1e-3) / 1e9, 1),
             "quantize_act_hbm_frac": round(act_bytes / (qa * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "device_copy_GBps": copy_gbps,
+            "quantize_act_copy_frac": round(act_bytes / (qa * 1e-3) / 1e9 / copy_gbps, 4),
             "gemm_ms": round(gemm_ms, 4),
             "gemm_ms_p10_p50_p90": percentiles(g_ms),
             "step_ms_p10_p50_p90": percentiles([a + b for a, b in zip(q_ms, g_ms)]),
