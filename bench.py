@@ -254,15 +254,15 @@ def mfma_probe(torch, mx, dev, a_codes, b_codes, iters=2000, reps=10):
 
 def workload_roofline(layers, flop, ms):
     """Where a workload stands against its bound, per step at time ms:
-    algorithmic HBM bytes (bf16 activations read, E4M3 + E8M0 codes written
-    and read back by the GEMM, weight codes + scales, f16 bias, bf16 output)
-    against 8 TB/s, and 2*M*N*K against the 5.0 PFLOP/s dense MXFP8 peak. The
-    bound is the one with the larger time at peak (HBM for the 128-token
-    linear, MFMA for the others)."""
+    algorithmic HBM bytes (bf16 activations read, weight codes + scales, f16
+    bias, bf16 output; the activation codes that the quantizer writes and the
+    GEMM reads back are this implementation's, not the linear's, and are not
+    counted) against 8 TB/s, and 2*M*N*K against the 5.0 PFLOP/s dense MXFP8
+    peak. The bound is the one with the larger time at peak (HBM for the
+    128-token linear, MFMA for the others)."""
     nbytes = 0
     for shp, _, _ in layers:
-        act = shp.M * shp.K
-        nbytes += act * 2 + 2 * (act + act // 32)  # bf16 in; codes + scales written, then read
+        nbytes += shp.M * shp.K * 2  # bf16 activations in
         nbytes += shp.N * shp.K + shp.N * shp.K // 32 + shp.N * 2 + shp.M * shp.N * 2
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
     t_mfma = flop / (PEAK_MXFP8_TFLOPS * 1e12)
