@@ -179,8 +179,9 @@ int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int6
  * workgroup per (tile, range), writing fp32 partial sums into a workspace;
  * a second kernel adds the ranges in order 0, 1, ..., adds the bias, applies
  * the epilogue and rounds to bf16. The reduction order is fixed, so results
- * are deterministic; with splits = 1 they equal mx_linear_slab bit for bit,
- * otherwise the fp32 sums are associated differently (same tolerance).
+ * are deterministic; splits = 1 runs mx_linear_slab's kernel (same bits, no
+ * workspace used), otherwise the fp32 sums are associated differently (same
+ * tolerance).
  * ------------------------------------------------------------------------ */
 
 /* Workspace bytes for mx_linear_slab_splitk: splits * T * 256 KiB with
@@ -208,7 +209,8 @@ int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64
  * streams each weight row once per K range while the token slab stays in
  * the L2, instead of padding the tokens to 256. K is split into `splits`
  * ranges: splits = 1 writes y directly, bit-identical to mx_linear_slab (the
- * same chain of MFMAs in K order, the same epilogue); splits > 1 writes fp32
+ * same chain of MFMAs in K order, started at the bias, and the same
+ * epilogue); splits > 1 writes fp32
  * partials [splits][M][N] that a second kernel adds in range order before
  * bias, epilogue and bf16: fixed order, deterministic, the tolerance of
  * mx_linear_slab. */

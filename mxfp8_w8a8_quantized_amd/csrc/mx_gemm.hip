@@ -1307,6 +1307,9 @@ hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int6
 hipError_t launch_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
                                      const uint8_t* ws, int64_t N, const void* bias, int epi, void* y, int splits,
                                      float* part, hipStream_t stream) {
+  // One range is the plain kernel itself (its accumulators start at the
+  // bias; the split form adds the bias after the ranges).
+  if (splits == 1) return launch_linear_slab(xq, xs, M, K, wq, ws, N, bias, epi, y, stream);
   Params p;
   p.x = xq;
   p.xs = xs;

@@ -159,15 +159,16 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
     }
   };
 
-  // One accumulator, slabs in K order: with one range the result is the
-  // slab GEMM's bit for bit (the same chain of MFMAs). A slab past the range
-  // (the second of the last step when nh is odd) was loaded as zero codes:
-  // its MFMA adds exact zeros to an accumulator that is never -0 (it starts
-  // at +0), so it leaves it unchanged.
+  // One accumulator, slabs in K order, started at the bias for the direct
+  // output (at zero for partial sums): with one range the result is the slab
+  // GEMM's bit for bit (the same chain of MFMAs from the same start). The
+  // slab past the range (the second of the last step when nh is odd, loaded
+  // as zero codes) is not multiplied, so the chain has exactly nh MFMAs.
   f32x16 acc = f32x16{};
-  auto mma = [&](const Pair& F) {
+  auto mma = [&](const Pair& F, int t) {
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.s[0].a, F.s[0].b, acc, 0, 0, 0, F.s[0].sa, 0, F.s[0].sb);
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.s[1].a, F.s[1].b, acc, 0, 0, 0, F.s[1].sa, 0, F.s[1].sb);
+    if (2 * t + 1 < nh)
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.s[1].a, F.s[1].b, acc, 0, 0, 0, F.s[1].sa, 0, F.s[1].sb);
   };
   // Step t (ring slot t % RP, fragment set t % 3): its MFMAs on fragments
   // read two steps earlier, then wait for step t + 2's slabs (this wave's
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
   Pair F[3];
   auto step = [&](int t, auto k) {
     constexpr int K = decltype(k)::value;
-    mma(F[K % 3]);
+    mma(F[K % 3], t);
     if (t + 2 < np) {
       if (nload == 2)
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((RP - 3) * 4) : "memory");
@@ -191,9 +192,8 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
   };
 
   // The bias quads of this lane's outputs (direct output only), loaded
-  // before the first slabs so that their round trip overlaps the K loop.
-  // They are older than every slab load, so the slab waits below (loads
-  // complete in order) cover them too.
+  // before the first slabs; they are older than every slab load, so the
+  // first slabs' wait below (loads complete in order) covers them too.
   i32x2 bq[4];
   if constexpr (!PART) {
     const bool has_b = p.bias != nullptr;
@@ -209,6 +209,18 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
   else
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RP - 2) * 2) : "memory");
   __builtin_amdgcn_s_barrier();
+  if constexpr (!PART) {
+    // The bias (landed with the first slabs): lane holds n = n0 + 32 wf +
+    // 8 q + 4 (lane/32) + r in element 4 q + r.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w0 = (uint32_t)bq[q][0], w1 = (uint32_t)bq[q][1];
+      acc[4 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xFFFFu));
+      acc[4 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16));
+      acc[4 * q + 2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 & 0xFFFFu));
+      acc[4 * q + 3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16));
+    }
+  }
   read(F[0], std::integral_constant<int, 0>{});
   read(F[1], std::integral_constant<int, 1>{});
   for (int t = 0; t < np; t += RP) {
@@ -237,14 +249,9 @@ __global__ __launch_bounds__(512, 1) void small_kernel(SmallParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int n = n0 + 32 * wf + 8 * q + 4 * hi;
-      const uint32_t w0 = (uint32_t)bq[q][0], w1 = (uint32_t)bq[q][1];
-      const float b[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xFFFFu)),
-                          (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)),
-                          (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 & 0xFFFFu)),
-                          (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16))};
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[4 * q + r] + b[r]);
+      for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[4 * q + r]);
       const bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
       const bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
       const int off = (m_ok && n < p.N) ? ((m - m0) * p.N + n) * 2 : kDrop;
