@@ -22,7 +22,8 @@ kernels behind the C ABI:
   are too few to occupy the GPU, the slab GEMM for the video tokens).
 * The feed-forward pair quantizes its input into the workspace, runs
   ffn.net.0.proj with the requantizing epilogue (the MX slab of its bf16 GELU
-  output, never written as bf16) and ffn.net.2 on that slab.
+  output, never written as bf16) and ffn.net.2 on that slab through its plan
+  (mx_linear_slab_auto: tuned by ``tune()``, else the default rule).
 
 The parts of a block that are not quantized linears (norms, modulation,
 attention itself, residual adds) are not here: the caller hands in the
@@ -31,7 +32,7 @@ activation each linear reads, by input role (``ROLES``).
 
 import torch
 
-from . import Slab, mx_linear, mx_linear_slab, mx_linear_slab_requant, mx_linear_tune, mx_linear_tune_ws_bytes
+from . import Slab, mx_linear, mx_linear_slab_auto, mx_linear_slab_requant, mx_linear_tune, mx_linear_tune_ws_bytes
 from . import mx_linear_ws_bytes, mx_quantize_act_slab, mx_quantize_weight_slab, mx_slab_rows, plan_lookup
 
 # Input role of each GEMM of a block, in call order, with the linears it
@@ -82,8 +83,12 @@ class DenoiseStepLinears:
         # slab first (also the feed-forward input, viewed as a slab below),
         # then what the shape's plan needs.
         ws = max(mx_linear_ws_bytes(M, K, N) for gemm, M, K, N, _ in self.shapes() if gemm != "ffn.net.2")
-        if ws < 0:
-            raise ValueError("hidden must be a multiple of 64")
+        if ws < 0 or mx_linear_tune_ws_bytes(tokens, ffn, hidden) < 0:
+            raise ValueError("hidden and ffn must be multiples of 64")
+        # ffn.net.2 reads the intermediate slab, so any plan's partial sums
+        # for it fit the whole workspace (the up-projection is done with the
+        # activation slab at its start by then).
+        ws = max(ws, mx_linear_tune_ws_bytes(tokens, ffn, hidden))
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=self.device)
         self.ffn_input = self._slab_view(tokens)
         self.tuned = {}
@@ -149,41 +154,52 @@ class DenoiseStepLinears:
                 mx_quantize_act_slab(inputs[role], self.ffn_input)
                 mx_linear_slab_requant(self.ffn_input, w, b, gelu=gelu, out=self.ffn_hidden)
             elif gemm == "ffn.net.2":
-                mx_linear_slab(self.ffn_hidden, w, b, gelu=gelu, y=self.outputs[gemm])
+                mx_linear_slab_auto(self.ffn_hidden, w, b, gelu=gelu, y=self.outputs[gemm], workspace=self.workspace)
             else:
                 mx_linear(inputs[role], w, b, gelu=gelu, y=self.outputs[gemm], workspace=self.workspace)
 
     def tune(self, inputs, block=0, reps=5):
-        """Warm-up tuning (mx_linear_tune) of the one-call GEMMs of a block on
-        block `block`'s weights and the given inputs: each shape's candidate
-        kernels are timed once and the fastest is cached for the process, so
-        every later run() takes it. Synchronizes; returns {gemm: plan} with
-        the plan each GEMM runs from now on (its default where not tuned)."""
+        """Warm-up tuning (mx_linear_tune) of the planned GEMMs of a block on
+        block `block`'s weights and the given inputs (ffn.net.2 on the
+        intermediate slab the up-projection writes from them): each shape's
+        candidate kernels are timed once and the fastest is cached for the
+        process, so every later run() takes it. Synchronizes; returns
+        {gemm: plan} with the plan each GEMM runs from now on."""
         slabs = self.weights[block]
         if slabs is None:
             raise RuntimeError(f"block {block} has no weights (set_block)")
         self._check_inputs(inputs)
         tune_ws = None
         for gemm, role, _, gelu in GEMMS:
-            if gemm in ("ffn.net.0.proj", "ffn.net.2"):
-                continue  # the requantizing pair runs the slab GEMM itself
+            if gemm == "ffn.net.0.proj":
+                continue  # the requantizing epilogue runs the slab GEMM itself
             w, b = slabs[gemm]
-            M, K, N = self.rows[role], self.hidden, w.rows
+            if gemm == "ffn.net.2":
+                # on the intermediate slab that the up-projection writes
+                w1, b1 = slabs["ffn.net.0.proj"]
+                mx_quantize_act_slab(inputs["ffn"], self.ffn_input)
+                mx_linear_slab_requant(self.ffn_input, w1, b1, gelu=True, out=self.ffn_hidden)
+                xs, M, K = self.ffn_hidden, self.tokens, self.ffn
+            else:
+                M, K = self.rows[role], self.hidden
+                xs = self._slab_view(M)
+                mx_quantize_act_slab(inputs[role], xs)
+            N = w.rows
             need = max(mx_linear_tune_ws_bytes(M, K, N), 1)
             if tune_ws is None or tune_ws.numel() < need:
                 tune_ws = torch.empty((need,), dtype=torch.uint8, device=self.device)
-            xs = self._slab_view(M)
-            mx_quantize_act_slab(inputs[role], xs)
             self.tuned[gemm] = mx_linear_tune(xs, w, b, gelu=gelu, y=self.outputs[gemm], workspace=tune_ws,
                                               reps=reps)
         del tune_ws
         return self.plans()
 
     def plans(self):
-        """{gemm: (kind, splits)} each one-call GEMM runs with (mx_linear's
-        plan lookup: tuned, else the default rule)."""
+        """{gemm: (kind, splits)} each planned GEMM runs with (the plan
+        lookup of mx_linear and mx_linear_slab_auto: tuned, else the default
+        rule); ffn.net.0.proj always runs the slab kernel with the
+        requantizing epilogue."""
         return {gemm: plan_lookup(M, K, N, gelu) for gemm, M, K, N, gelu in self.shapes()
-                if gemm not in ("ffn.net.0.proj", "ffn.net.2")}
+                if gemm != "ffn.net.0.proj"}
 
     def run(self, inputs):
         """Enqueue the whole step: every block's linears, in block order."""
