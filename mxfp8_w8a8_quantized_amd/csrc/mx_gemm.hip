@@ -648,10 +648,18 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
 namespace slab {
 
 constexpr int NT4 = 256;
-constexpr int R_W = 0, R_X = 16384, R_WS = 32768, R_XS = 33280;
-constexpr int REGION = 33792;
+constexpr int R_W = 0, R_X = 16384;
+constexpr int REGION = 32768;  // codes of one half-step: 256 rows x 64 B, both operands
 constexpr int LDS = 4 * REGION;
-constexpr int LOADS_PER_HALF = 9;  // per wave: 4 + 4 code DMAs, 1 scale DMA
+// Scale ring past the code regions: [weights, tokens][8 half-steps][256
+// rows][2 groups], 512 bytes per operand and half-step. The scales of two
+// consecutive half-steps (an even one and the next) sit side by side, so one
+// 1 KB DMA fetches both: one scale DMA per wave every other half-step
+// instead of one every half-step (each DMA instruction costs about the same
+// whatever its size, and the scales are 3% of the bytes).
+constexpr int SR = LDS;
+constexpr int SR_OP = 8 * 512;
+constexpr int CODE_LOADS = 8;  // per wave and half-step: 4 + 4 code DMAs of 1 KB
 
 struct Src {
   const uint8_t* w;  // tile origin in slab 0: codes, then scales
@@ -663,30 +671,48 @@ struct Src {
   int voff;                 // lane part of a code DMA offset
 };
 
-// Loads of half-step j by wave `wave` (0..3): 16-row blocks 4 wave ..
-// 4 wave + 3 of both code operands (1 KB each; lane L takes row L/4, global
-// chunk (L%4) ^ (L/16) into LDS slot L%4) and one 256-byte half of the
-// weight (waves 0, 1) or token (waves 2, 3) scales.
-template <bool PC>
-__device__ __forceinline__ void issue_half(const Src& S, uint8_t* smem, int j, int wave, int lane) {
+// Code loads of half-step j by wave `wave` (0..3): 16-row blocks 4 wave ..
+// 4 wave + 3 of both operands (1 KB each; lane L takes row L/4, global
+// chunk (L%4) ^ (L/16) into LDS slot L%4).
+__device__ __forceinline__ void issue_codes(const Src& S, uint8_t* smem, int j, int wave) {
   uint8_t* reg = smem + (j & 3) * REGION;
-  const bool valid = j < S.nh;
-  const uint32_t nc = valid ? 16384u : 0u, ns = valid ? 512u : 0u;
+  const uint32_t nc = j < S.nh ? 16384u : 0u;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(S.w + (uint64_t)j * S.w_slab, nc);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x + (uint64_t)j * S.x_slab, nc);
-  if constexpr (!PC) {
-    const bool wscale = wave < 2;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(wscale ? S.ws + (uint64_t)j * (S.w_slab >> 5) : S.xs + (uint64_t)j * (S.x_slab >> 5), ns);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(reg + (wscale ? R_WS : R_XS) + (wave & 1) * 256), 4,
-                                             lane * 4, (wave & 1) * 256, 0, 0);
-  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = wave * 4 + u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(reg + R_W + q * 1024), 16, S.voff, q * 1024, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
   }
+}
+
+// Scales of half-steps s and s + 1 (s even) of one operand into ring slots
+// s % 8 and s % 8 + 1: lanes 0..31 take half-step s's 512 bytes, lanes
+// 32..63 half-step s + 1's (the next scale slab, `stride` bytes on). Waves 0
+// and 1 both copy the weight scales, waves 2 and 3 the token scales (the
+// same bytes to the same place, so every wave issues one DMA and all waves
+// keep equal load counts). Half-steps past the range read zeros.
+__device__ __forceinline__ void issue_scales(const Src& S, uint8_t* smem, int s, int wave, int lane) {
+  const bool wop = wave < 2;
+  const uint32_t stride = (uint32_t)((wop ? S.w_slab : S.x_slab) >> 5);
+  const uint32_t n = s + 1 < S.nh ? stride + 512u : (s < S.nh ? 512u : 0u);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc((wop ? S.ws : S.xs) + (uint64_t)s * stride, n);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(smem + SR + (wop ? 0 : SR_OP) + (s & 7) * 512), 16,
+                                           (lane & 31) * 16 + (lane >> 5) * stride, 0, 0, 0);
+}
+
+// The prologue's loads in the order the loop would have issued them (the
+// scales of half-steps 0, 1 and 2, 3 each before the codes of the first of
+// the pair): the loop's waits count on that order.
+template <bool PC>
+__device__ __forceinline__ void issue_prologue(const Src& S, uint8_t* smem, int wave, int lane) {
+  if constexpr (!PC) issue_scales(S, smem, 0, wave, lane);
+  issue_codes(S, smem, 0, wave);
+  issue_codes(S, smem, 1, wave);
+  if constexpr (!PC) issue_scales(S, smem, 2, wave, lane);
+  issue_codes(S, smem, 2, wave);
+  issue_codes(S, smem, 3, wave);
 }
 
 struct Frags {
@@ -701,6 +727,7 @@ struct Frags {
 // the 64, and the scale of group l/32 of the half-step.
 template <bool PC>
 __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn, int wm, int lane) {
+  // reg is region 0 (the LDS base): half-step 0, scale ring slot 0.
   const int r32 = lane & 31, hi = lane >> 5;
   const int sw = (r32 >> 2) & 3;
   const int c0 = (hi ^ sw) << 4, c1 = ((2 + hi) ^ sw) << 4;
@@ -710,7 +737,7 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
     const uint8_t* ra = reg + R_W + row * 64;
     const i32x4 a0 = *(const i32x4*)(ra + c0), a1 = *(const i32x4*)(ra + c1);
     F.a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    F.sa[f] = PC ? 127 : reg[R_WS + row * 2 + hi];
+    F.sa[f] = PC ? 127 : reg[SR + row * 2 + hi];
   }
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
@@ -718,7 +745,7 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
     const uint8_t* rb = reg + R_X + row * 64;
     const i32x4 b0 = *(const i32x4*)(rb + c0), b1 = *(const i32x4*)(rb + c1);
     F.b[f] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    F.sb[f] = PC ? 127 : reg[R_XS + row * 2 + hi];
+    F.sb[f] = PC ? 127 : reg[SR + SR_OP + row * 2 + hi];
   }
 }
 
@@ -743,7 +770,7 @@ __device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const Frags& F) {
 // (0..23): r < 16 a 16-byte code half (fragment r / 4 of A for r % 4 < 2,
 // else of B; r % 2 picks the half), r >= 16 a scale byte (16..19 A, 20..23
 // B). Load piece d (0..8): d < 8 one 1 KB code DMA (d even: weights, odd:
-// tokens, block 4 wave + d / 2), d = 8 the scale DMA.
+// tokens, block 4 wave + d / 2), d = 8 the scale DMA (even half-steps).
 struct FragAddr {
   const uint8_t* a;  // row wn*128 + l%32 of the weight codes
   const uint8_t* b;  // row wm*128 + l%32 of the token codes
@@ -752,16 +779,20 @@ struct FragAddr {
   const uint8_t* sb;
 };
 
-__device__ __forceinline__ FragAddr frag_addr(const uint8_t* reg, int wn, int wm, int lane) {
+// Addresses of half-step h's fragments: codes in region h % 4, scales in
+// ring slot h % 8.
+__device__ __forceinline__ FragAddr frag_addr(const uint8_t* smem, int h, int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
   const int sw = (r32 >> 2) & 3;
+  const uint8_t* reg = smem + (h & 3) * REGION;
+  const uint8_t* sc = smem + SR + (h & 7) * 512;
   FragAddr A;
   A.a = reg + R_W + (wn * 128 + r32) * 64;
   A.b = reg + R_X + (wm * 128 + r32) * 64;
   A.c0 = (hi ^ sw) << 4;
   A.c1 = ((2 + hi) ^ sw) << 4;
-  A.sa = reg + R_WS + (wn * 128 + r32) * 2 + hi;
-  A.sb = reg + R_XS + (wm * 128 + r32) * 2 + hi;
+  A.sa = sc + (wn * 128 + r32) * 2 + hi;
+  A.sb = sc + SR_OP + (wm * 128 + r32) * 2 + hi;
   return A;
 }
 
@@ -785,33 +816,27 @@ __device__ __forceinline__ void read_piece(Frags& F, const FragAddr& A) {
 }
 
 struct LoadRes {
-  __amdgpu_buffer_rsrc_t w, x, s;
+  __amdgpu_buffer_rsrc_t w, x;
   uint8_t* reg;
 };
 
-__device__ __forceinline__ LoadRes load_res(const Src& S, uint8_t* smem, int j, int wave) {
+__device__ __forceinline__ LoadRes load_res(const Src& S, uint8_t* smem, int j) {
   LoadRes L;
   L.reg = smem + (j & 3) * REGION;
-  const bool valid = j < S.nh;
-  const uint32_t nc = valid ? 16384u : 0u, ns = valid ? 512u : 0u;
+  const uint32_t nc = j < S.nh ? 16384u : 0u;
   L.w = make_rsrc(S.w + (uint64_t)j * S.w_slab, nc);
   L.x = make_rsrc(S.x + (uint64_t)j * S.x_slab, nc);
-  L.s = make_rsrc(wave < 2 ? S.ws + (uint64_t)j * (S.w_slab >> 5) : S.xs + (uint64_t)j * (S.x_slab >> 5), ns);
   return L;
 }
 
+// Code piece D (0..7) of the refill of half-step j + 4.
 template <int D>
-__device__ __forceinline__ void load_piece(const LoadRes& L, const Src& S, int wave, int lane) {
-  if constexpr (D < 8) {
-    const int q = wave * 4 + D / 2;
-    if constexpr ((D & 1) == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.w, (lds_ptr)(L.reg + R_W + q * 1024), 16, S.voff, q * 1024, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.x, (lds_ptr)(L.reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.s, (lds_ptr)(L.reg + (wave < 2 ? R_WS : R_XS) + (wave & 1) * 256), 4,
-                                             lane * 4, (wave & 1) * 256, 0, 0);
-  }
+__device__ __forceinline__ void load_piece(const LoadRes& L, const Src& S, int wave) {
+  const int q = wave * 4 + D / 2;
+  if constexpr ((D & 1) == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.w, (lds_ptr)(L.reg + R_W + q * 1024), 16, S.voff, q * 1024, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.x, (lds_ptr)(L.reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
 }
 
 // Reads and loads issued in MFMA slot i (0..15): reads 12i/5 .. 12(i+1)/5 - 1
@@ -831,9 +856,11 @@ struct Slot {
 };
 
 // Per-channel FP8 has no block scales: read pieces 16..23 and load piece 8
-// (the scale DMA) drop out; the other pieces keep their slots.
+// (the scale DMA) drop out; the other pieces keep their slots. Loads a wave
+// has issued after half-step h + 1's codes, at the top of half-step h: those
+// of half-steps h - 2 and h - 1, one of them even (2 x 8 codes + 1 scale DMA).
 template <bool PC>
-constexpr int loads_per_half() { return PC ? LOADS_PER_HALF - 1 : LOADS_PER_HALF; }
+constexpr int loads_two_halves() { return PC ? 2 * CODE_LOADS : 2 * CODE_LOADS + 1; }
 template <bool PC, int R>
 constexpr bool has_read() { return !PC || R < 16; }
 template <bool PC, int I>
@@ -842,8 +869,8 @@ constexpr int slot_reads() {
   for (int r = Slot<I>::r0; r < Slot<I>::r1; ++r) n += (!PC || r < 16) ? 1 : 0;
   return n;
 }
-template <bool PC, int I>
-constexpr bool slot_dma() { return Slot<I>::d >= 0 && !(PC && Slot<I>::d == 8); }
+template <bool PC, bool EVEN, int I>
+constexpr bool slot_dma() { return Slot<I>::d >= 0 && !(Slot<I>::d == 8 && (PC || !EVEN)); }
 
 // Half-step j. The lgkmcnt(0) in the wait keeps any wave's refill from
 // overtaking another wave's last reads of the region being refilled. The LDS
@@ -852,16 +879,17 @@ constexpr bool slot_dma() { return Slot<I>::d >= 0 && !(PC && Slot<I>::d == 8); 
 // compiler keeps them in that order (it cannot tell the regions apart), and
 // the scheduling groups put each slot's reads and DMA behind one MFMA: with
 // one wave per SIMD, this is what keeps the MFMA pipe fed and the address
-// path free of bursts.
-template <bool PC>
+// path free of bursts. EVEN: j is even, and the scales of half-steps j + 4
+// and j + 5 are fetched too (slot 0).
+template <bool PC, bool EVEN>
 __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
                                           int j, int wave, int wn, int wm, int lane) {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * loads_per_half<PC>()) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(loads_two_halves<PC>()) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  const FragAddr A = frag_addr(smem + ((j + 1) & 3) * REGION, wn, wm, lane);
-  const LoadRes L = load_res(S, smem, j + 4, wave);
+  const FragAddr A = frag_addr(smem, j + 1, wn, wm, lane);
+  const LoadRes L = load_res(S, smem, j + 4);
   static_for<0, 16>([&](auto I) {
     constexpr int i = decltype(I)::value;
     using SL = Slot<i>;
@@ -869,14 +897,19 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
       constexpr int r = decltype(Rr)::value;
       if constexpr (has_read<PC, r>()) read_piece<r>(nxt, A);
     });
-    if constexpr (slot_dma<PC, i>()) load_piece<SL::d>(L, S, wave, lane);
+    if constexpr (slot_dma<PC, EVEN, i>()) {
+      if constexpr (SL::d == 8)
+        issue_scales(S, smem, j + 4, wave, lane);
+      else
+        load_piece<SL::d>(L, S, wave);
+    }
   });
   mma16<PC>(acc, cur);
   static_for<0, 16>([&](auto I) {
     constexpr int i = decltype(I)::value;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if constexpr (slot_reads<PC, i>() > 0) __builtin_amdgcn_sched_group_barrier(0x100, slot_reads<PC, i>(), 0);
-    if constexpr (slot_dma<PC, i>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // its DMA
+    if constexpr (slot_dma<PC, EVEN, i>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // its DMA
   });
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -981,8 +1014,8 @@ __device__ __forceinline__ void store_tile_part(const f32x16 (&acc)[4][4], const
 // epilogue from a 2 KB LDS table past the ring: [0, 256) weight rows n0..,
 // [256, 512) token rows m0..).
 enum { OUT_Y = 0, OUT_Q = 1, OUT_PART = 2, OUT_PCY = 3 };
-constexpr int PC_TABLE = LDS;  // byte offset of the per-channel scale table
-constexpr int LDS_PC = LDS + 2048;
+constexpr int PC_TABLE = SR + 2 * SR_OP;  // byte offset of the per-channel scale table
+constexpr int LDS_PC = PC_TABLE + 2048;
 // Bias: each wave copies the 128 f16 bias values of its weight-row half (wn)
 // into its own 256-byte LDS slot past the ring and the per-channel table,
 // with one 4-byte DMA per lane issued before the ring's first stages; waiting
@@ -1000,7 +1033,7 @@ constexpr int BIAS_TABLE = LDS_PC;
 constexpr int LDS_OUT = LDS_PC + 4 * 256;
 
 template <int OUT>
-constexpr int lds_bytes() { return OUT == OUT_PART ? LDS : LDS_OUT; }
+constexpr int lds_bytes() { return LDS_OUT; }
 
 __device__ __forceinline__ void issue_bias_slot(const Params& p, uint8_t* smem, int n0, int rows_n, int wave, int wn,
                                                 int lane) {
@@ -1063,13 +1096,14 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
 
   constexpr bool BIAS_IN_ACC = OUT == OUT_Y || OUT == OUT_Q;
   if constexpr (OUT != OUT_PART) issue_bias_slot(p, smem, n0, rows_n, wave, wn, lane);
-  issue_half<PC>(S, smem, 0, wave, lane);
-  issue_half<PC>(S, smem, 1, wave, lane);
-  issue_half<PC>(S, smem, 2, wave, lane);
-  issue_half<PC>(S, smem, 3, wave, lane);
+  issue_prologue<PC>(S, smem, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
+  // Loads issued after the bias: 4 x 8 codes (+ 2 scale DMAs); after half-step
+  // 0's codes: 3 x 8 codes (+ 1 scale DMA).
+  constexpr int AFTER_BIAS = 4 * CODE_LOADS + (PC ? 0 : 2);
+  constexpr int AFTER_H0 = 3 * CODE_LOADS + (PC ? 0 : 1);
   if constexpr (BIAS_IN_ACC) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(4 * loads_per_half<PC>()) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(AFTER_BIAS) : "memory");
     BiasQuads B0;
     read_bias_quads(B0, smem, wave, lane);
 #pragma unroll
@@ -1090,7 +1124,7 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
       for (int jj = 0; jj < 4; ++jj) asm volatile("" : "+a"(acc[i][jj]));
     __builtin_amdgcn_sched_barrier(0);
   }
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * loads_per_half<PC>()) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(AFTER_H0) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   Frags F0, F1;
@@ -1098,10 +1132,10 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   const int nh = S.nh;
   int j = 0;
   for (; j + 1 < nh; j += 2) {
-    half_step<PC>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
-    half_step<PC>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
+    half_step<PC, true>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+    half_step<PC, false>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
   }
-  if (j < nh) half_step<PC>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+  if (j < nh) half_step<PC, true>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
   __builtin_amdgcn_sched_barrier(0);
   BiasQuads B;
   if constexpr (OUT == OUT_PCY) read_bias_quads(B, smem, wave, lane);
