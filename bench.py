@@ -46,6 +46,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -75,10 +76,17 @@ CONTEXT = {
 
 
 def kernel_source_hash():
+    """Hash of the GEMM sources' code: comments dropped and whitespace runs
+    folded (neither source puts // or /* in a string), so that a comment edit
+    keeps the committed counters valid and any code edit voids them."""
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "mxfp8_w8a8_quantized_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mxfp8_w8a8_quantized_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -643,8 +643,9 @@ hipError_t launch(const Params& p, int nwg, hipStream_t st) {
 //
 // Region layout: weight codes 256 rows x 64 B, 16-byte chunk c of row r at
 // slot c ^ ((r >> 2) & 3) (conflict-free for 16-lane phases of b128 reads);
-// token codes the same; then the scales of both, [row][2] bytes. Loads past
-// the last half-step use an empty resource and write zeros that nobody reads.
+// token codes the same. The block scales of both operands sit in a ring of
+// their own past the four regions (below). Loads past the last half-step use
+// an empty resource and write zeros that nobody reads.
 namespace slab {
 
 constexpr int NT4 = 256;
@@ -842,10 +843,10 @@ __device__ __forceinline__ void load_piece(const LoadRes& L, const Src& S, int w
 // Reads and loads issued in MFMA slot i (0..15): reads 12i/5 .. 12(i+1)/5 - 1
 // in slots 0..9 (24 reads, the fragments the next half-step's first MFMAs
 // need first), none in slots 10..15, and one DMA in each of slots 0..8 (the
-// scale DMA first), so the refill of j+4 leaves early and has the most time
-// to land. Finishing the reads six MFMAs (about 380 cycles) before the end
-// of the half-step lets them complete before the next half-step's
-// lgkmcnt(0) and barrier, so the MFMA pipe does not drain there: 2% faster
+// scale DMA first, on even half-steps), so the refill of j+4 leaves early
+// and has the most time to land. Finishing the reads six MFMAs (about 380
+// cycles) before the end of the half-step lets them complete before the next
+// half-step's lgkmcnt(0) and barrier, so the MFMA pipe does not drain there: 2% faster
 // than spreading them over all 16 slots (reads over 8, 12 or 14 slots:
 // within 1% of 10). Placing the DMAs in every other slot or in the middle
 // slots measured the same within 1%.
