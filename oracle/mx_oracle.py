@@ -8,9 +8,9 @@ What the layer computes, and where that is stated:
 
 * Model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)", section
   "Quantization Details": weights and activations are 8-bit of data type
-  ``mx_fp`` with ``group_size`` 32 for both, symmetric, activations quantized
-  dynamically at run time; weights are stored as FP8 E4M3 with one E8M0 scale
-  per 32 elements; the biases of the quantized linears are F16.
+  ``mx_fp`` with ``group_size`` 32 for both, symmetric, and the activation
+  side is quantized on the fly; the checkpoint keeps E4M3 codes for the
+  weights plus an E8M0 exponent for each run of 32 of them, and F16 biases.
 * "Model Quantization Techniques" (LightX2V), section "MiniMax-H3 Video VAE
   Encoder Conv3D", mode table: the FP8 mode with FP32 accumulation uses the
   full E4M3 range, qmax 448 for weights and activations.
