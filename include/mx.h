@@ -408,11 +408,12 @@ int mx_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int
 /* ------------------------------------------------------------------------
  * Per-output-channel FP8: the second FP8 scheme of the pages ("Wan2.2 I2V
  * A14B, four-step 720p: native LightX2V FP8 and NVFP4", section "Conversion
- * and compatibility": E4M3 weights with per-output-channel FP32 scales,
- * nearest rounding; "Model Quantization Techniques", mode table: channel-
- * symmetric FP8 weights, channel-dynamic-symmetric FP8 activations with the
- * row scale max(abs(x)) / qmax, qmax 448 with FP32 accumulation). One f32
- * scale per row instead of one E8M0 scale per 32 elements:
+ * and compatibility": E4M3 weight codes scaled by one FP32 factor per
+ * output channel, rounded to nearest; "Model Quantization Techniques", mode
+ * table: FP8 weights symmetric per channel, FP8 activations symmetric per
+ * row and computed on the fly as max(abs(x)) / qmax, qmax 448, FP32
+ * accumulation). One f32 scale per row instead of one E8M0 scale per 32
+ * elements:
  *   s    = f32(max_k |x[r][k]|) / 448        (f32 division, nearest even)
  *   code = E4M3(f32(x[r][k]) / s)            (f32 division, then nearest even,
  *                                             saturating at +-448, sign of
