@@ -3,9 +3,10 @@
 //   y[m][n] = bf16_rne( epi( sum_k xhat[m][k] * what[n][k] + f32(bias[n]) ) )
 //
 // (model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)", section
-// "Quantization Details": W8A8 MXFP8 linears, E4M3 with per-32 E8M0 scales,
-// dynamic activations, F16 biases; FP32 accumulation as in the FP32-accum
-// FP8 mode of "Model Quantization Techniques", Conv3D mode table.)
+// "Quantization Details": W8A8 MXFP8 linears, E4M3 codes under one E8M0
+// exponent per 32 elements, activations quantized on the fly, F16 biases;
+// FP32 accumulation as in the FP32-accum FP8 mode of "Model Quantization
+// Techniques", Conv3D mode table.)
 //
 // Three kernels, all with 256 (weight rows n) x 256 (tokens m) output tiles,
 // the weights as the MFMA's A operand (a lane's accumulators are consecutive

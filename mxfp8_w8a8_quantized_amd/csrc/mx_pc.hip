@@ -1,11 +1,11 @@
 // Per-output-channel FP8 quantizer: one FP32 scale per row, E4M3 codes.
 //
 // Scheme ("Wan2.2 I2V A14B, four-step 720p: native LightX2V FP8 and NVFP4",
-// section "Conversion and compatibility": E4M3 weights with per-output-
-// channel FP32 scales, nearest rounding; "Model Quantization Techniques",
-// mode table: channel-symmetric FP8 weights and channel-dynamic-symmetric FP8
-// activations, row scale = max(abs(x)) / qmax, qmax 448 with FP32
-// accumulation):
+// section "Conversion and compatibility": E4M3 weight codes scaled by one
+// FP32 factor per output channel, rounded to nearest; "Model Quantization
+// Techniques", mode table: FP8 weights symmetric per channel, FP8
+// activations symmetric per row and computed on the fly, row scale =
+// max(abs(x)) / qmax, qmax 448, FP32 accumulation):
 //   s    = fp32(max |x[r, :]|) / 448            (FP32 division, nearest even)
 //   code = E4M3(fp32(x) / s)                   (FP32 division, then nearest
 //                                               even, saturating at +-448)
