@@ -695,13 +695,29 @@ __device__ __forceinline__ void issue_codes(const Src& S, uint8_t* smem, int j, 
 // and 1 both copy the weight scales, waves 2 and 3 the token scales (the
 // same bytes to the same place, so every wave issues one DMA and all waves
 // keep equal load counts). Half-steps past the range read zeros.
-__device__ __forceinline__ void issue_scales(const Src& S, uint8_t* smem, int s, int wave, int lane) {
+struct ScaleLoad {
+  __amdgpu_buffer_rsrc_t r;
+  uint8_t* dst;
+  uint32_t voff;
+};
+
+__device__ __forceinline__ ScaleLoad scale_res(const Src& S, uint8_t* smem, int s, int wave, int lane) {
   const bool wop = wave < 2;
   const uint32_t stride = (uint32_t)((wop ? S.w_slab : S.x_slab) >> 5);
   const uint32_t n = s + 1 < S.nh ? stride + 512u : (s < S.nh ? 512u : 0u);
-  const __amdgpu_buffer_rsrc_t r = make_rsrc((wop ? S.ws : S.xs) + (uint64_t)s * stride, n);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(smem + SR + (wop ? 0 : SR_OP) + (s & 7) * 512), 16,
-                                           (lane & 31) * 16 + (lane >> 5) * stride, 0, 0, 0);
+  ScaleLoad L;
+  L.r = make_rsrc((wop ? S.ws : S.xs) + (uint64_t)s * stride, n);
+  L.dst = smem + SR + (wop ? 0 : SR_OP) + (s & 7) * 512;
+  L.voff = (lane & 31) * 16 + (lane >> 5) * stride;
+  return L;
+}
+
+__device__ __forceinline__ void issue_scale_load(const ScaleLoad& L) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(L.r, (lds_ptr)L.dst, 16, L.voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void issue_scales(const Src& S, uint8_t* smem, int s, int wave, int lane) {
+  issue_scale_load(scale_res(S, smem, s, wave, lane));
 }
 
 // The prologue's loads in the order the loop would have issued them (the
@@ -753,18 +769,17 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
 
 // Per-channel FP8 (PC) runs the same MFMAs with unit block scales (E8M0
 // 127 = 2^0); its row scales are applied in the epilogue.
-template <bool PC>
+// MFMAs t = B .. E - 1 of a half-step (t = 4 i + j: weight fragment i,
+// token fragment j).
+template <bool PC, int B = 0, int E = 16>
 __device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const Frags& F) {
-  static_for<0, 4>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    static_for<0, 4>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      if constexpr (PC)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-      else
-        acc[i][j] =
-            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, F.sa[i], 0, F.sb[j]);
-    });
+  static_for<B, E>([&](auto T) {
+    constexpr int i = decltype(T)::value / 4, j = decltype(T)::value % 4;
+    if constexpr (PC)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    else
+      acc[i][j] =
+          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, F.sa[i], 0, F.sb[j]);
   });
 }
 
@@ -841,16 +856,24 @@ __device__ __forceinline__ void load_piece(const LoadRes& L, const Src& S, int w
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.x, (lds_ptr)(L.reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
 }
 
-// Reads and loads issued in MFMA slot i (0..15): reads 12i/5 .. 12(i+1)/5 - 1
-// in slots 0..9 (24 reads, the fragments the next half-step's first MFMAs
-// need first), none in slots 10..15, and one DMA in each of slots 0..8 (the
-// scale DMA first, on even half-steps), so the refill of j+4 leaves early
-// and has the most time to land. Finishing the reads six MFMAs (about 380
-// cycles) before the end of the half-step lets them complete before the next
-// half-step's lgkmcnt(0) and barrier, so the MFMA pipe does not drain there: 2% faster
-// than spreading them over all 16 slots (reads over 8, 12 or 14 slots:
-// within 1% of 10). Placing the DMAs in every other slot or in the middle
-// slots measured the same within 1%.
+// MFMAs of a half-step issued ahead of its wait and barrier, and the most
+// set-up instructions scheduled behind each of them. Against none (the
+// set-up after the barrier): one 0.9% slower, two 1.8% faster, three and
+// four 2.4-4.3% faster on the Wan shapes, five and six a little below
+// three.
+constexpr int PRE_MFMAS = 3;
+constexpr int SETUP_PER_MFMA = 11;
+
+// Reads and loads issued in slot i, the i-th MFMA after the barrier (0 ..
+// 15 - PRE_MFMAS): reads 12i/5 .. 12(i+1)/5 - 1 in slots 0..9 (24 reads, the
+// fragments the next half-step's first MFMAs need first), none after, and
+// one DMA in each of slots 0..8 (the scale DMA first, on even half-steps),
+// so the refill of j+4 leaves early and has the most time to land.
+// Finishing the reads six MFMAs (about 380 cycles) before the next
+// half-step's lgkmcnt(0) lets them complete before it, so the MFMA pipe
+// does not drain there: 2% faster than spreading them over every slot
+// (reads over 8, 12 or 14 slots: within 1% of 10). Placing the DMAs in every
+// other slot or in the middle slots measured the same within 1%.
 template <int I>
 struct Slot {
   static constexpr int r0 = I < 10 ? 12 * I / 5 : 24, r1 = I < 10 ? 12 * (I + 1) / 5 : 24;  // reads [r0, r1)
@@ -887,11 +910,22 @@ template <bool PC, bool EVEN>
 __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
                                           int j, int wave, int wn, int wm, int lane) {
   __builtin_amdgcn_sched_barrier(0);
+  // The first MFMAs read registers only: issued ahead of the wait and the
+  // barrier, with the half-step's address set-up in their shadow, they keep
+  // the MFMA pipe busy through the wait, the barrier and the set-up.
+  const FragAddr A = frag_addr(smem, j + 1, wn, wm, lane);
+  const LoadRes L = load_res(S, smem, j + 4);
+  ScaleLoad SLd;
+  if constexpr (EVEN && !PC) SLd = scale_res(S, smem, j + 4, wave, lane);
+  mma16<PC, 0, PRE_MFMAS>(acc, cur);
+  static_for<0, PRE_MFMAS>([&](auto I) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x006, SETUP_PER_MFMA, 0);  // set-up VALU / SALU
+  });
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(loads_two_halves<PC>()) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  const FragAddr A = frag_addr(smem, j + 1, wn, wm, lane);
-  const LoadRes L = load_res(S, smem, j + 4);
   static_for<0, 16>([&](auto I) {
     constexpr int i = decltype(I)::value;
     using SL = Slot<i>;
@@ -901,13 +935,13 @@ __device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags
     });
     if constexpr (slot_dma<PC, EVEN, i>()) {
       if constexpr (SL::d == 8)
-        issue_scales(S, smem, j + 4, wave, lane);
+        issue_scale_load(SLd);
       else
         load_piece<SL::d>(L, S, wave);
     }
   });
-  mma16<PC>(acc, cur);
-  static_for<0, 16>([&](auto I) {
+  mma16<PC, PRE_MFMAS, 16>(acc, cur);
+  static_for<0, 16 - PRE_MFMAS>([&](auto I) {
     constexpr int i = decltype(I)::value;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if constexpr (slot_reads<PC, i>() > 0) __builtin_amdgcn_sched_group_barrier(0x100, slot_reads<PC, i>(), 0);
