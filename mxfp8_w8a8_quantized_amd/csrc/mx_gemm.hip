@@ -872,8 +872,10 @@ constexpr int SETUP_PER_MFMA = 11;
 // Finishing the reads six MFMAs (about 380 cycles) before the next
 // half-step's lgkmcnt(0) lets them complete before it, so the MFMA pipe
 // does not drain there: 2% faster than spreading them over every slot
-// (reads over 8, 12 or 14 slots: within 1% of 10). Placing the DMAs in every
-// other slot or in the middle slots measured the same within 1%.
+// (reads over 8, 12 or 14 of 16 slots: within 1% of 10; over 9, 11 or 13
+// slots with three MFMAs ahead of the barrier: the same or slower). Placing
+// the DMAs in every other slot, in the middle slots or one slot later
+// measured the same within 1%.
 template <int I>
 struct Slot {
   static constexpr int r0 = I < 10 ? 12 * I / 5 : 24, r1 = I < 10 ? 12 * (I + 1) / 5 : 24;  // reads [r0, r1)
