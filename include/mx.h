@@ -310,8 +310,9 @@ void mx_linear_plan_clear(void);
  * The linear in one call: the production entry point. What the model card
  * "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)" describes in
  * "Quantization Details" for each of its quantized linears: bf16 activations
- * quantized to MXFP8 at run time, multiplied against E4M3 weights with
- * per-32 E8M0 scales, F16 bias; FP32 accumulation, bf16 output:
+ * quantized to MXFP8 at run time, multiplied against E4M3 weight codes that
+ * carry one E8M0 scale per 32 elements, F16 bias; FP32 accumulation, bf16
+ * output:
  *   y[m][n] = bf16_rne( epi( sum_k xhat[m][k] * what[n][k] + f32(bias[n]) ) )
  * ------------------------------------------------------------------------ */
 
@@ -331,9 +332,8 @@ int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N);
  * than given gives way to the default one): two kernels on `stream` (the
  * quantizer, then the GEMM), plus the ordered reduction of the partial sums
  * for plans with several K ranges. Nothing is allocated. workspace: device
- * memory of
- * mx_linear_ws_bytes(M, K, N) bytes (at least what the chosen plan needs),
- * 256-byte aligned, not overlapping x, the weights, bias or y; its contents
+ * memory of mx_linear_ws_bytes(M, K, N) bytes (at least what the chosen
+ * plan needs), 256-byte aligned, not overlapping x, the weights, bias or y; its contents
  * are overwritten and need no initial value. K % 64 == 0, N % 16 == 0.
  * Results: deterministic; bit-identical to mx_quantize_act_slab +
  * mx_linear_slab_plan with the same plan. Errors: as mx_linear_slab, plus
