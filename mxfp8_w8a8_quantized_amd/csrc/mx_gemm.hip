@@ -57,7 +57,7 @@ constexpr int SCALE_BYTES = 4 * 256;        // one operand, one stage
 constexpr int LDS_BYTES = 4 * TILE_BYTES + 4 * SCALE_BYTES;
 constexpr int kDropOffset = 1 << 30;  // beyond every resource: the store is dropped
 constexpr int kStoreAux = 2;
-constexpr int64_t kMaxTailSplits = 8;  // as the split-K choice: partial traffic grows with it  // cache policy of the fast path's output stores: non-temporal
+constexpr int64_t kMaxTailSplits = 8;  // as the split-K choice: partial traffic grows with it
 
 struct Params {
   const uint8_t* x;   // bf16 tokens (fused) or E4M3 codes
