@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 11
+#define MX_ABI_VERSION 12
 
 typedef enum {
   MX_OK = 0,
@@ -158,6 +158,19 @@ int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                    const uint8_t* wq, const uint8_t* ws, int64_t N,
                    const void* bias, int epilogue, void* y, void* stream);
 
+/* mx_linear_slab on 256 (weight rows) x 128 (tokens) tiles: the same
+ * arguments, checks and result bit for bit (every output is the same chain
+ * of MFMAs from the bias), with twice as many tiles. For a few hundred tokens
+ * (the 512 text tokens of Wan2.2's attn2 k/v: 80 tiles of 256 x 256 on the
+ * MI355X's 256 CUs) the 256 x 256 tiles leave most CUs idle; this form
+ * fills more of them without splitting K, so there are no partial sums to
+ * write and reduce (model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound
+ * OptRTN)", section "Quantization Details": the cross-attention projections
+ * are among the quantized linears). */
+int mx_linear_slab_m128(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                        const uint8_t* wq, const uint8_t* ws, int64_t N,
+                        const void* bias, int epilogue, void* y, void* stream);
+
 /* The same linear, writing instead of y the MX quantization of bf16 y (by
  * the rule above, bit-identical to mx_quantize_act_slab of mx_linear_slab's
  * output) in the slab layout of an operand with rows M and K' = N:
@@ -242,16 +255,19 @@ int mx_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_
  * Per-shape plans. A plan names the kernel for one slab-linear shape and its
  * K split: MX_PLAN_SLAB (mx_linear_slab, splits 1), MX_PLAN_SPLITK
  * (mx_linear_slab_splitk), MX_PLAN_SMALL (mx_linear_slab_small),
- * MX_PLAN_BALANCED (mx_linear_slab_balanced, splits 1). Every plan computes
- * the same linear (same operands, tolerance and determinism; SLAB, and SPLITK
- * or SMALL with splits 1, bit-identical). The library keeps a process-local
+ * MX_PLAN_BALANCED (mx_linear_slab_balanced, splits 1), MX_PLAN_SLAB_M128
+ * (mx_linear_slab_m128, splits 1). Every plan computes the same linear (same
+ * operands, tolerance and determinism; SLAB, SLAB_M128, and SPLITK or SMALL
+ * with splits 1, bit-identical). The library keeps a process-local
  * cache of tuned plans keyed by (device, M, K, N, epilogue), guarded by a
  * mutex; mx_linear_tune fills it, mx_linear_slab_auto reads it.
  * ------------------------------------------------------------------------ */
-enum { MX_PLAN_SLAB = 0, MX_PLAN_SPLITK = 1, MX_PLAN_SMALL = 2, MX_PLAN_BALANCED = 3 };
+enum { MX_PLAN_SLAB = 0, MX_PLAN_SPLITK = 1, MX_PLAN_SMALL = 2, MX_PLAN_BALANCED = 3, MX_PLAN_SLAB_M128 = 4 };
 
 /* The rule used without tuning: MX_PLAN_SMALL with mx_linear_small_choose
- * splits for 1 <= M <= 256; else MX_PLAN_SPLITK with
+ * splits for 1 <= M <= 256; else MX_PLAN_SLAB_M128 when the 256 x 256 tiles
+ * number 32 to 128 (one round of twice as many 128-token tiles then keeps a
+ * quarter to all of an MI355X's 256 CUs busy); else MX_PLAN_SPLITK with
  * mx_linear_splitk_choose splits when that is above 1; else MX_PLAN_SLAB.
  * MX_ERR_INVALID_ARGUMENT on NULL outputs or a bad shape (M, N < 0; K not a
  * positive multiple of 64; sizes past the slab linear's limits). */
@@ -277,7 +293,8 @@ int64_t mx_linear_tune_ws_bytes(int64_t M, int64_t K, int64_t N);
  * reps <= 1000), queued behind a short delay kernel so that they run back to
  * back (GPU time, as under graph replay), and keeps the fastest. Candidates: the default plan; the
  * slab GEMM; split-K with 2, 3, 4, 6, 8 ranges when the 256 x 256 tiles are
- * fewer than the device's CUs; the few-token kernel with 1, 2, 3, 4, 6, 8
+ * fewer than the device's CUs; for M > 128 the 128-token tiles when the
+ * 256 x 256 tiles are fewer than twice the CUs; the few-token kernel with 1, 2, 3, 4, 6, 8
  * ranges for M <= 1024; the balanced GEMM when the tiles leave a partial
  * last round. Candidates whose workspace exceeds workspace_bytes, or that
  * their entry point rejects, are skipped. The choice is cached for (current

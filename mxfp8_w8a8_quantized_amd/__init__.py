@@ -27,7 +27,9 @@ MX_PLAN_SLAB = 0
 MX_PLAN_SPLITK = 1
 MX_PLAN_SMALL = 2
 MX_PLAN_BALANCED = 3
-PLAN_NAMES = {MX_PLAN_SLAB: "slab", MX_PLAN_SPLITK: "splitk", MX_PLAN_SMALL: "small", MX_PLAN_BALANCED: "balanced"}
+MX_PLAN_SLAB_M128 = 4
+PLAN_NAMES = {MX_PLAN_SLAB: "slab", MX_PLAN_SPLITK: "splitk", MX_PLAN_SMALL: "small", MX_PLAN_BALANCED: "balanced",
+              MX_PLAN_SLAB_M128: "slab_m128"}
 PLAN_KINDS = {v: k for k, v in PLAN_NAMES.items()}
 
 # Every symbol include/mx.h declares, with its ctypes signature.
@@ -49,6 +51,7 @@ SIGNATURES = {
     "mx_quantize_weight_slab": ([_P, _INT, _I64, _I64, _I64, _P, _P, _P], _INT),
     "mx_slab_pack": ([_P, _P, _I64, _I64, _P, _P, _P], _INT),
     "mx_linear_slab": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
+    "mx_linear_slab_m128": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P], _INT),
     "mx_linear_slab_requant": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P, _P, _P], _INT),
     "mx_linear_splitk_ws_bytes": ([_I64, _I64, _INT], _I64),
     "mx_linear_splitk_choose": ([_I64, _I64, _I64], _INT),
@@ -327,6 +330,16 @@ def _slab_linear_args(x, w, bias):
 
 def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
     """y = bf16(epi(xhat @ what^T + bias)) on slab operands x (tokens) and w (weights)."""
+    return _slab_call(lib().mx_linear_slab, x, w, bias, gelu, y)
+
+
+def mx_linear_slab_m128(x, w, bias=None, gelu=False, y=None):
+    """mx_linear_slab on 256 (weight rows) x 128 (tokens) tiles: the same y,
+    bit for bit, with twice the tiles (for a few hundred tokens)."""
+    return _slab_call(lib().mx_linear_slab_m128, x, w, bias, gelu, y)
+
+
+def _slab_call(fn, x, w, bias, gelu, y):
     dev, M, N, K = _slab_linear_args(x, w, bias)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
     _need(y, "y", torch.bfloat16, dev)
@@ -334,11 +347,7 @@ def mx_linear_slab(x, w, bias=None, gelu=False, y=None):
         raise ValueError("y must be bf16 [M, N]")
     epi = MX_EPI_GELU_TANH if gelu else MX_EPI_NONE
     with torch.cuda.device(dev):
-        _check(
-            lib().mx_linear_slab(
-                _ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _stream(dev)
-            )
-        )
+        _check(fn(_ptr(x.q), _ptr(x.s), M, K, _ptr(w.q), _ptr(w.s), N, _ptr(bias), epi, _ptr(y), _stream(dev)))
     return y
 
 

@@ -661,7 +661,22 @@ constexpr int LDS = 4 * REGION;
 // whatever its size, and the scales are 3% of the bytes).
 constexpr int SR = LDS;
 constexpr int SR_OP = 8 * 512;
-constexpr int CODE_LOADS = 8;  // per wave and half-step: 4 + 4 code DMAs of 1 KB
+
+// Tile shapes. The tile is 256 weight rows x 64 JB tokens: four waves of 128
+// (n) x 32 JB (m), each holding 4 x JB accumulator blocks of 32 x 32. JB = 4
+// (256 x 256 tiles) is the GEMM of every large shape; JB = 2 (256 x 128)
+// doubles the tile count for a few hundred tokens, where the 256 x 256 tiles
+// would leave most CUs idle (the 512-token linear: 80 tiles on 256 CUs),
+// without the partial sums of a K split. Both use the same LDS layout (the
+// token half of each region only partly filled when JB = 2).
+template <int JB>
+struct Shape {
+  static constexpr int MT = 64 * JB;           // tokens per tile
+  static constexpr int CODE_LOADS = 4 + JB;    // code DMAs of 1 KB per wave and half-step
+  static constexpr int NMFMA = 4 * JB;         // MFMAs per wave and half-step
+  static constexpr int NCODE = 8 + 2 * JB;     // 16-byte code reads per wave and half-step
+  static constexpr int NREAD = NCODE + 4 + JB;  // and the scale bytes
+};
 
 struct Src {
   const uint8_t* w;  // tile origin in slab 0: codes, then scales
@@ -673,19 +688,24 @@ struct Src {
   int voff;                 // lane part of a code DMA offset
 };
 
-// Code loads of half-step j by wave `wave` (0..3): 16-row blocks 4 wave ..
-// 4 wave + 3 of both operands (1 KB each; lane L takes row L/4, global
-// chunk (L%4) ^ (L/16) into LDS slot L%4).
+// Code loads of half-step j by wave `wave` (0..3): 16-row weight blocks
+// 4 wave .. 4 wave + 3 and token blocks JB wave .. JB wave + JB - 1 (1 KB
+// each; lane L takes row L/4, global chunk (L%4) ^ (L/16) into LDS slot L%4),
+// in the order of the loop's load pieces.
+template <int JB>
 __device__ __forceinline__ void issue_codes(const Src& S, uint8_t* smem, int j, int wave) {
   uint8_t* reg = smem + (j & 3) * REGION;
   const uint32_t nc = j < S.nh ? 16384u : 0u;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(S.w + (uint64_t)j * S.w_slab, nc);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x + (uint64_t)j * S.x_slab, nc);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x + (uint64_t)j * S.x_slab, JB == 4 ? nc : nc / 4 * JB);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = wave * 4 + u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(reg + R_W + q * 1024), 16, S.voff, q * 1024, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
+    if (u < JB) {
+      const int qx = wave * JB + u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(reg + R_X + qx * 1024), 16, S.voff, qx * 1024, 0, 0);
+    }
   }
 }
 
@@ -694,21 +714,26 @@ __device__ __forceinline__ void issue_codes(const Src& S, uint8_t* smem, int j, 
 // 32..63 half-step s + 1's (the next scale slab, `stride` bytes on). Waves 0
 // and 1 both copy the weight scales, waves 2 and 3 the token scales (the
 // same bytes to the same place, so every wave issues one DMA and all waves
-// keep equal load counts). Half-steps past the range read zeros.
+// keep equal load counts). Half-steps past the range read zeros. With JB = 2
+// a half-step's token scales are 256 bytes: lanes 0..15 and 32..47 fetch
+// them, lanes 16..31 and 48..63 repeat those bytes into the slots' unused
+// upper halves.
 struct ScaleLoad {
   __amdgpu_buffer_rsrc_t r;
   uint8_t* dst;
   uint32_t voff;
 };
 
+template <int JB>
 __device__ __forceinline__ ScaleLoad scale_res(const Src& S, uint8_t* smem, int s, int wave, int lane) {
   const bool wop = wave < 2;
   const uint32_t stride = (uint32_t)((wop ? S.w_slab : S.x_slab) >> 5);
-  const uint32_t n = s + 1 < S.nh ? stride + 512u : (s < S.nh ? 512u : 0u);
+  const uint32_t one = JB == 4 || wop ? 512u : 256u;  // bytes of one half-step
+  const uint32_t n = s + 1 < S.nh ? stride + one : (s < S.nh ? one : 0u);
   ScaleLoad L;
   L.r = make_rsrc((wop ? S.ws : S.xs) + (uint64_t)s * stride, n);
   L.dst = smem + SR + (wop ? 0 : SR_OP) + (s & 7) * 512;
-  L.voff = (lane & 31) * 16 + (lane >> 5) * stride;
+  L.voff = (JB == 4 || wop ? (lane & 31) : (lane & 15)) * 16 + (lane >> 5) * stride;
   return L;
 }
 
@@ -716,35 +741,37 @@ __device__ __forceinline__ void issue_scale_load(const ScaleLoad& L) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(L.r, (lds_ptr)L.dst, 16, L.voff, 0, 0, 0);
 }
 
+template <int JB>
 __device__ __forceinline__ void issue_scales(const Src& S, uint8_t* smem, int s, int wave, int lane) {
-  issue_scale_load(scale_res(S, smem, s, wave, lane));
+  issue_scale_load(scale_res<JB>(S, smem, s, wave, lane));
 }
 
 // The prologue's loads in the order the loop would have issued them (the
 // scales of half-steps 0, 1 and 2, 3 each before the codes of the first of
 // the pair): the loop's waits count on that order.
-template <bool PC>
+template <bool PC, int JB>
 __device__ __forceinline__ void issue_prologue(const Src& S, uint8_t* smem, int wave, int lane) {
-  if constexpr (!PC) issue_scales(S, smem, 0, wave, lane);
-  issue_codes(S, smem, 0, wave);
-  issue_codes(S, smem, 1, wave);
-  if constexpr (!PC) issue_scales(S, smem, 2, wave, lane);
-  issue_codes(S, smem, 2, wave);
-  issue_codes(S, smem, 3, wave);
+  if constexpr (!PC) issue_scales<JB>(S, smem, 0, wave, lane);
+  issue_codes<JB>(S, smem, 0, wave);
+  issue_codes<JB>(S, smem, 1, wave);
+  if constexpr (!PC) issue_scales<JB>(S, smem, 2, wave, lane);
+  issue_codes<JB>(S, smem, 2, wave);
+  issue_codes<JB>(S, smem, 3, wave);
 }
 
+template <int JB>
 struct Frags {
-  i32x8 a[4];  // weights: rows wn*128 + 32 f + l%32
-  i32x8 b[4];  // tokens:  rows wm*128 + 32 f + l%32
+  i32x8 a[4];   // weights: rows wn*128 + 32 f + l%32
+  i32x8 b[JB];  // tokens:  rows wm*32*JB + 32 f + l%32
   int sa[4];
-  int sb[4];
+  int sb[JB];
 };
 
 // Fragments of a region for the 32x32x64 MFMA: lane l, fragment f reads row
 // base + 32 f + l%32, K bytes [16 (l/32), +16) and [32 + 16 (l/32), +16) of
 // the 64, and the scale of group l/32 of the half-step.
-template <bool PC>
-__device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn, int wm, int lane) {
+template <bool PC, int JB>
+__device__ __forceinline__ void read_frags(Frags<JB>& F, const uint8_t* reg, int wn, int wm, int lane) {
   // reg is region 0 (the LDS base): half-step 0, scale ring slot 0.
   const int r32 = lane & 31, hi = lane >> 5;
   const int sw = (r32 >> 2) & 3;
@@ -758,8 +785,8 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
     F.sa[f] = PC ? 127 : reg[SR + row * 2 + hi];
   }
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int row = wm * 128 + 32 * f + r32;
+  for (int f = 0; f < JB; ++f) {
+    const int row = wm * 32 * JB + 32 * f + r32;
     const uint8_t* rb = reg + R_X + row * 64;
     const i32x4 b0 = *(const i32x4*)(rb + c0), b1 = *(const i32x4*)(rb + c1);
     F.b[f] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -769,12 +796,12 @@ __device__ __forceinline__ void read_frags(Frags& F, const uint8_t* reg, int wn,
 
 // Per-channel FP8 (PC) runs the same MFMAs with unit block scales (E8M0
 // 127 = 2^0); its row scales are applied in the epilogue.
-// MFMAs t = B .. E - 1 of a half-step (t = 4 i + j: weight fragment i,
+// MFMAs t = B .. E - 1 of a half-step (t = JB i + j: weight fragment i,
 // token fragment j).
-template <bool PC, int B = 0, int E = 16>
-__device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const Frags& F) {
+template <bool PC, int JB, int B, int E>
+__device__ __forceinline__ void mma16(f32x16 (&acc)[4][JB], const Frags<JB>& F) {
   static_for<B, E>([&](auto T) {
-    constexpr int i = decltype(T)::value / 4, j = decltype(T)::value % 4;
+    constexpr int i = decltype(T)::value / JB, j = decltype(T)::value % JB;
     if constexpr (PC)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
     else
@@ -784,10 +811,13 @@ __device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const Frags& F) {
 }
 
 // Pieces of a half-step, for interleaving in program order. Read piece r
-// (0..23): r < 16 a 16-byte code half (fragment r / 4 of A for r % 4 < 2,
-// else of B; r % 2 picks the half), r >= 16 a scale byte (16..19 A, 20..23
-// B). Load piece d (0..8): d < 8 one 1 KB code DMA (d even: weights, odd:
-// tokens, block 4 wave + d / 2), d = 8 the scale DMA (even half-steps).
+// (0 .. NREAD - 1): r < 4 JB a 16-byte code half of fragment r / 4 (of A
+// for r % 4 < 2, else of B; r % 2 picks the half); 4 JB <= r < NCODE a half
+// of A fragment JB + (r - 4 JB) / 2 (JB = 2 only); then the scale bytes, 4 of
+// A and JB of B. Load piece d (0 .. CODE_LOADS - 1) one 1 KB code DMA: for
+// JB = 4 weights for d even, tokens for d odd (block 4 wave + d / 2, resp.
+// JB wave + d / 2); for JB = 2 weights, tokens, weights, tokens, weights,
+// weights. The scale DMA (even half-steps) is scheduled apart.
 struct FragAddr {
   const uint8_t* a;  // row wn*128 + l%32 of the weight codes
   const uint8_t* b;  // row wm*128 + l%32 of the token codes
@@ -798,6 +828,7 @@ struct FragAddr {
 
 // Addresses of half-step h's fragments: codes in region h % 4, scales in
 // ring slot h % 8.
+template <int JB>
 __device__ __forceinline__ FragAddr frag_addr(const uint8_t* smem, int h, int wn, int wm, int lane) {
   const int r32 = lane & 31, hi = lane >> 5;
   const int sw = (r32 >> 2) & 3;
@@ -805,30 +836,33 @@ __device__ __forceinline__ FragAddr frag_addr(const uint8_t* smem, int h, int wn
   const uint8_t* sc = smem + SR + (h & 7) * 512;
   FragAddr A;
   A.a = reg + R_W + (wn * 128 + r32) * 64;
-  A.b = reg + R_X + (wm * 128 + r32) * 64;
+  A.b = reg + R_X + (wm * 32 * JB + r32) * 64;
   A.c0 = (hi ^ sw) << 4;
   A.c1 = ((2 + hi) ^ sw) << 4;
   A.sa = sc + (wn * 128 + r32) * 2 + hi;
-  A.sb = sc + SR_OP + (wm * 128 + r32) * 2 + hi;
+  A.sb = sc + SR_OP + (wm * 32 * JB + r32) * 2 + hi;
   return A;
 }
 
-template <int R>
-__device__ __forceinline__ void read_piece(Frags& F, const FragAddr& A) {
-  if constexpr (R < 16) {
-    constexpr int f = R / 4, part = R % 4;
+template <int R, int JB>
+__device__ __forceinline__ void read_piece(Frags<JB>& F, const FragAddr& A) {
+  constexpr int NC = Shape<JB>::NCODE;
+  if constexpr (R < NC) {
+    // Fragment f of A (part 0, 1) or of B (part 2, 3); part % 2: the half.
+    constexpr int f = R < 4 * JB ? R / 4 : JB + (R - 4 * JB) / 2;
+    constexpr int part = R < 4 * JB ? R % 4 : (R - 4 * JB) % 2;
     const uint8_t* base = (part < 2 ? A.a : A.b) + 32 * f * 64;
     const i32x4 v = *(const i32x4*)(base + ((part & 1) ? A.c1 : A.c0));
-    i32x8& d = part < 2 ? F.a[f] : F.b[f];
+    i32x8& d = part < 2 ? F.a[f] : F.b[f < JB ? f : 0];
     if constexpr ((part & 1) == 0) {
       d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
     } else {
       d[4] = v[0]; d[5] = v[1]; d[6] = v[2]; d[7] = v[3];
     }
-  } else if constexpr (R < 20) {
-    F.sa[R - 16] = A.sa[32 * (R - 16) * 2];
+  } else if constexpr (R < NC + 4) {
+    F.sa[R - NC] = A.sa[32 * (R - NC) * 2];
   } else {
-    F.sb[R - 20] = A.sb[32 * (R - 20) * 2];
+    F.sb[R - NC - 4] = A.sb[32 * (R - NC - 4) * 2];
   }
 }
 
@@ -837,23 +871,28 @@ struct LoadRes {
   uint8_t* reg;
 };
 
+template <int JB>
 __device__ __forceinline__ LoadRes load_res(const Src& S, uint8_t* smem, int j) {
   LoadRes L;
   L.reg = smem + (j & 3) * REGION;
   const uint32_t nc = j < S.nh ? 16384u : 0u;
   L.w = make_rsrc(S.w + (uint64_t)j * S.w_slab, nc);
-  L.x = make_rsrc(S.x + (uint64_t)j * S.x_slab, nc);
+  L.x = make_rsrc(S.x + (uint64_t)j * S.x_slab, JB == 4 ? nc : nc / 4 * JB);
   return L;
 }
 
-// Code piece D (0..7) of the refill of half-step j + 4.
-template <int D>
+// Code piece D (0 .. CODE_LOADS - 1) of the refill of half-step j + 4.
+template <int D, int JB>
 __device__ __forceinline__ void load_piece(const LoadRes& L, const Src& S, int wave) {
-  const int q = wave * 4 + D / 2;
-  if constexpr ((D & 1) == 0)
+  constexpr bool W = (D & 1) == 0 || D >= 2 * JB;  // a weight block, else a token block
+  constexpr int u = D < 2 * JB ? D / 2 : D - JB;    // its index among the wave's blocks
+  if constexpr (W) {
+    const int q = wave * 4 + u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.w, (lds_ptr)(L.reg + R_W + q * 1024), 16, S.voff, q * 1024, 0, 0);
-  else
+  } else {
+    const int q = wave * JB + u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.x, (lds_ptr)(L.reg + R_X + q * 1024), 16, S.voff, q * 1024, 0, 0);
+  }
 }
 
 // MFMAs of a half-step issued ahead of its wait and barrier, and the most
@@ -875,29 +914,46 @@ constexpr int SETUP_PER_MFMA = 11;
 // (reads over 8, 12 or 14 of 16 slots: within 1% of 10; over 9, 11 or 13
 // slots with three MFMAs ahead of the barrier: the same or slower). Placing
 // the DMAs in every other slot, in the middle slots or one slot later
-// measured the same within 1%.
-template <int I>
+// measured the same within 1%. Slot i issues the DMAs [d0, d1) of the list
+// (the scale DMA, then the code pieces 0, 1, ...): for JB = 4 one in each of
+// slots 0..8; for JB = 2 (8 MFMAs, 5 slots after the barrier) the 18 reads
+// in slots 0..3 and the 7 DMAs spread over slots 0..4.
+template <int I, int JB>
 struct Slot {
-  static constexpr int r0 = I < 10 ? 12 * I / 5 : 24, r1 = I < 10 ? 12 * (I + 1) / 5 : 24;  // reads [r0, r1)
-  static constexpr int d = I < 9 ? (I == 0 ? 8 : I - 1) : -1;  // load piece, or none
+  static constexpr int NS = JB == 4 ? 10 : 4;  // slots holding reads
+  static constexpr int NR = Shape<JB>::NREAD;
+  static constexpr int r0 = I < NS ? NR * I / NS : NR, r1 = I < NS ? NR * (I + 1) / NS : NR;  // reads [r0, r1)
+  static constexpr int ND = Shape<JB>::CODE_LOADS + 1;  // DMAs in the list
+  static constexpr int DS = JB == 4 ? ND : 5;            // slots holding DMAs
+  static constexpr int d0 = JB == 4 ? (I < ND ? I : ND) : (I < DS ? ND * I / DS : ND);
+  static constexpr int d1 = JB == 4 ? (I < ND ? I + 1 : ND) : (I < DS ? ND * (I + 1) / DS : ND);
 };
 
-// Per-channel FP8 has no block scales: read pieces 16..23 and load piece 8
-// (the scale DMA) drop out; the other pieces keep their slots. Loads a wave
-// has issued after half-step h + 1's codes, at the top of half-step h: those
-// of half-steps h - 2 and h - 1, one of them even (2 x 8 codes + 1 scale DMA).
-template <bool PC>
-constexpr int loads_two_halves() { return PC ? 2 * CODE_LOADS : 2 * CODE_LOADS + 1; }
-template <bool PC, int R>
-constexpr bool has_read() { return !PC || R < 16; }
-template <bool PC, int I>
+// Per-channel FP8 has no block scales: the scale read pieces and the scale
+// DMA drop out; the other pieces keep their slots. Loads a wave has issued
+// after half-step h + 1's codes, at the top of half-step h: those of
+// half-steps h - 2 and h - 1, one of them even (2 x CODE_LOADS codes + 1
+// scale DMA).
+template <bool PC, int JB>
+constexpr int loads_two_halves() { return PC ? 2 * Shape<JB>::CODE_LOADS : 2 * Shape<JB>::CODE_LOADS + 1; }
+template <bool PC, int R, int JB>
+constexpr bool has_read() { return !PC || R < Shape<JB>::NCODE; }
+template <bool PC, int I, int JB>
 constexpr int slot_reads() {
   int n = 0;
-  for (int r = Slot<I>::r0; r < Slot<I>::r1; ++r) n += (!PC || r < 16) ? 1 : 0;
+  for (int r = Slot<I, JB>::r0; r < Slot<I, JB>::r1; ++r) n += (!PC || r < Shape<JB>::NCODE) ? 1 : 0;
   return n;
 }
-template <bool PC, bool EVEN, int I>
-constexpr bool slot_dma() { return Slot<I>::d >= 0 && !(Slot<I>::d == 8 && (PC || !EVEN)); }
+// DMA k of the list is issued on this half-step (the scale DMA only on even
+// half-steps of the MX GEMM).
+template <bool PC, bool EVEN, int K>
+constexpr bool dma_on() { return K > 0 || (EVEN && !PC); }
+template <bool PC, bool EVEN, int I, int JB>
+constexpr int slot_dmas() {
+  int n = 0;
+  for (int k = Slot<I, JB>::d0; k < Slot<I, JB>::d1; ++k) n += (k > 0 || (EVEN && !PC)) ? 1 : 0;
+  return n;
+}
 
 // Half-step j. The lgkmcnt(0) in the wait keeps any wave's refill from
 // overtaking another wave's last reads of the region being refilled. The LDS
@@ -908,46 +964,51 @@ constexpr bool slot_dma() { return Slot<I>::d >= 0 && !(Slot<I>::d == 8 && (PC |
 // one wave per SIMD, this is what keeps the MFMA pipe fed and the address
 // path free of bursts. EVEN: j is even, and the scales of half-steps j + 4
 // and j + 5 are fetched too (slot 0).
-template <bool PC, bool EVEN>
-__device__ __forceinline__ void half_step(f32x16 (&acc)[4][4], Frags& cur, Frags& nxt, const Src& S, uint8_t* smem,
-                                          int j, int wave, int wn, int wm, int lane) {
+template <bool PC, bool EVEN, int JB>
+__device__ __forceinline__ void half_step(f32x16 (&acc)[4][JB], Frags<JB>& cur, Frags<JB>& nxt, const Src& S,
+                                          uint8_t* smem, int j, int wave, int wn, int wm, int lane) {
+  constexpr int NM = Shape<JB>::NMFMA;
   __builtin_amdgcn_sched_barrier(0);
   // The first MFMAs read registers only: issued ahead of the wait and the
   // barrier, with the half-step's address set-up in their shadow, they keep
   // the MFMA pipe busy through the wait, the barrier and the set-up.
-  const FragAddr A = frag_addr(smem, j + 1, wn, wm, lane);
-  const LoadRes L = load_res(S, smem, j + 4);
+  const FragAddr A = frag_addr<JB>(smem, j + 1, wn, wm, lane);
+  const LoadRes L = load_res<JB>(S, smem, j + 4);
   ScaleLoad SLd;
-  if constexpr (EVEN && !PC) SLd = scale_res(S, smem, j + 4, wave, lane);
-  mma16<PC, 0, PRE_MFMAS>(acc, cur);
+  if constexpr (EVEN && !PC) SLd = scale_res<JB>(S, smem, j + 4, wave, lane);
+  mma16<PC, JB, 0, PRE_MFMAS>(acc, cur);
   static_for<0, PRE_MFMAS>([&](auto I) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x006, SETUP_PER_MFMA, 0);  // set-up VALU / SALU
   });
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(loads_two_halves<PC>()) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(loads_two_halves<PC, JB>()) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  static_for<0, 16>([&](auto I) {
+  static_for<0, NM - PRE_MFMAS>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    using SL = Slot<i>;
+    using SL = Slot<i, JB>;
     static_for<SL::r0, SL::r1>([&](auto Rr) {
       constexpr int r = decltype(Rr)::value;
-      if constexpr (has_read<PC, r>()) read_piece<r>(nxt, A);
+      if constexpr (has_read<PC, r, JB>()) read_piece<r, JB>(nxt, A);
     });
-    if constexpr (slot_dma<PC, EVEN, i>()) {
-      if constexpr (SL::d == 8)
-        issue_scale_load(SLd);
-      else
-        load_piece<SL::d>(L, S, wave);
-    }
+    static_for<SL::d0, SL::d1>([&](auto Dk) {
+      constexpr int k = decltype(Dk)::value;
+      if constexpr (k == 0) {
+        if constexpr (dma_on<PC, EVEN, 0>()) issue_scale_load(SLd);
+      } else {
+        load_piece<k - 1, JB>(L, S, wave);
+      }
+    });
   });
-  mma16<PC, PRE_MFMAS, 16>(acc, cur);
-  static_for<0, 16 - PRE_MFMAS>([&](auto I) {
+  mma16<PC, JB, PRE_MFMAS, NM>(acc, cur);
+  static_for<0, NM - PRE_MFMAS>([&](auto I) {
     constexpr int i = decltype(I)::value;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if constexpr (slot_reads<PC, i>() > 0) __builtin_amdgcn_sched_group_barrier(0x100, slot_reads<PC, i>(), 0);
-    if constexpr (slot_dma<PC, EVEN, i>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // its DMA
+    if constexpr (slot_reads<PC, i, JB>() > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, slot_reads<PC, i, JB>(), 0);
+    if constexpr (slot_dmas<PC, EVEN, i, JB>() > 0)
+      __builtin_amdgcn_sched_group_barrier(0x020, slot_dmas<PC, EVEN, i, JB>(), 0);  // its DMAs
   });
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -1091,10 +1152,13 @@ __device__ __forceinline__ void read_bias_quads(BiasQuads& B, const uint8_t* sme
   for (int k = 0; k < 16; ++k) B.v[k] = *(const i32x2*)(base + (32 * (k >> 2) + 8 * (k & 3)) * 2);
 }
 
-template <int EPI, int OUT>
+template <int EPI, int OUT, int JB = 4>
 __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
+  static_assert(JB == 4 || (JB == 2 && OUT == OUT_Y), "128-token tiles have the bf16 output only");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr bool PC = OUT == OUT_PCY;
+  constexpr int MT = Shape<JB>::MT;
+  constexpr int CL = Shape<JB>::CODE_LOADS;
   int tm, tn;
   int bid = blockIdx.x, ks = 0;
   if constexpr (OUT == OUT_PART) {
@@ -1102,8 +1166,8 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
     bid /= p.splits;  // the partial tile, numbered within this launch
   }
   tile_coords(p.tile_base + bid, p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_m = min(p.M - m0, BM);
+  const int m0 = tm * MT, n0 = tn * BN;
+  const int rows_m = min(p.M - m0, MT);
   const int rows_n = min(p.N - n0, BN);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1118,7 +1182,8 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   }
   Src S;
   S.w_slab = (uint64_t)p.tiles_n * BN * 64;
-  S.x_slab = (uint64_t)p.tiles_m * BM * 64;
+  // Token slab rows: the slab layout's row count (a multiple of 256).
+  S.x_slab = JB == 4 ? (uint64_t)p.tiles_m * BM * 64 : (uint64_t)((p.tiles_m * MT + 255) & ~255) * 64;
   S.w = p.wq + (size_t)n0 * 64 + h0 * S.w_slab;
   S.x = p.x + (size_t)m0 * 64 + h0 * S.x_slab;
   S.ws = PC ? nullptr : p.ws + (size_t)n0 * 2 + h0 * (S.w_slab >> 5);
@@ -1126,20 +1191,20 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   S.nh = nh_wg;
   S.voff = (lane >> 2) * 64 + (((lane & 3) ^ (lane >> 4)) << 4);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < JB; ++j) acc[i][j] = f32x16{};
 
   constexpr bool BIAS_IN_ACC = OUT == OUT_Y || OUT == OUT_Q;
   if constexpr (OUT != OUT_PART) issue_bias_slot(p, smem, n0, rows_n, wave, wn, lane);
-  issue_prologue<PC>(S, smem, wave, lane);
+  issue_prologue<PC, JB>(S, smem, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  // Loads issued after the bias: 4 x 8 codes (+ 2 scale DMAs); after half-step
-  // 0's codes: 3 x 8 codes (+ 1 scale DMA).
-  constexpr int AFTER_BIAS = 4 * CODE_LOADS + (PC ? 0 : 2);
-  constexpr int AFTER_H0 = 3 * CODE_LOADS + (PC ? 0 : 1);
+  // Loads issued after the bias: 4 x CL codes (+ 2 scale DMAs); after
+  // half-step 0's codes: 3 x CL codes (+ 1 scale DMA).
+  constexpr int AFTER_BIAS = 4 * CL + (PC ? 0 : 2);
+  constexpr int AFTER_H0 = 3 * CL + (PC ? 0 : 1);
   if constexpr (BIAS_IN_ACC) {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(AFTER_BIAS) : "memory");
     BiasQuads B0;
@@ -1152,28 +1217,28 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
         for (int r = 0; r < 4; ++r) {
           const float b = bias_at(B0, 4 * i + q, r);
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[i][jj][4 * q + r] = b;
+          for (int jj = 0; jj < JB; ++jj) acc[i][jj][4 * q + r] = b;
         }
     // Materialize the accumulators here, inside the first stage's latency
     // (left alone, the compiler moves their writes past the barrier below).
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) asm volatile("" : "+a"(acc[i][jj]));
+      for (int jj = 0; jj < JB; ++jj) asm volatile("" : "+a"(acc[i][jj]));
     __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(AFTER_H0) : "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  Frags F0, F1;
-  read_frags<PC>(F0, smem, wn, wm, lane);
+  Frags<JB> F0, F1;
+  read_frags<PC, JB>(F0, smem, wn, wm, lane);
   const int nh = S.nh;
   int j = 0;
   for (; j + 1 < nh; j += 2) {
-    half_step<PC, true>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
-    half_step<PC, false>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
+    half_step<PC, true, JB>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+    half_step<PC, false, JB>(acc, F1, F0, S, smem, j + 1, wave, wn, wm, lane);
   }
-  if (j < nh) half_step<PC, true>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
+  if (j < nh) half_step<PC, true, JB>(acc, F0, F1, S, smem, j, wave, wn, wm, lane);
   __builtin_amdgcn_sched_barrier(0);
   BiasQuads B;
   if constexpr (OUT == OUT_PCY) read_bias_quads(B, smem, wave, lane);
@@ -1198,8 +1263,8 @@ __global__ __launch_bounds__(NT4, 1) void linear_slab_kernel(Params p) {
   else if constexpr (OUT == OUT_PART)
     store_tile_part(acc, p, bid, ks, m0, wave, wm, lane);
   else
-    pp::store_tile8<EPI, 4, PC, BIAS_IN_ACC>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane,
-                                             (const float*)(smem + PC_TABLE));
+    pp::store_tile8<EPI, JB, PC, BIAS_IN_ACC>(acc, B, p, smem + wave * 32768, m0, n0, rows_m, rows_n, wn, wm, lane,
+                                              (const float*)(smem + PC_TABLE));
 }
 
 // Split-K reduction: one thread per 16-byte chunk of the partial tiles (the
@@ -1241,10 +1306,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Params p) {
   *(i32x2*)(p.y + (size_t)m * p.N + n) = i32x2{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1)};
 }
 
-template <int EPI, int OUT = OUT_Y>
+template <int EPI, int OUT = OUT_Y, int JB = 4>
 hipError_t launch(const Params& p, int nwg, hipStream_t st) {
   static bool configured = false;  // per instantiation; benign race (idempotent)
-  auto kern = linear_slab_kernel<EPI, OUT>;
+  auto kern = linear_slab_kernel<EPI, OUT, JB>;
   constexpr int lds = lds_bytes<OUT>();
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1347,6 +1412,33 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
   p.tiles_n = (int)((N + BN - 1) / BN);
   const int nwg = p.tiles_m * p.tiles_n;
   return epi == 1 ? slab::launch<1>(p, nwg, stream) : slab::launch<0>(p, nwg, stream);
+}
+
+hipError_t launch_linear_slab_m128(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,
+                                   const uint8_t* ws, int64_t N, const void* bias, int epi, void* y,
+                                   hipStream_t stream) {
+  Params p;
+  p.x = xq;
+  p.xs = xs;
+  p.wq = wq;
+  p.ws = ws;
+  p.bias = (const uint16_t*)bias;
+  p.y = (uint16_t*)y;
+  p.hq = nullptr;
+  p.hs = nullptr;
+  p.part = nullptr;
+  p.sx = nullptr;
+  p.sw = nullptr;
+  p.splits = 1;
+  p.tile_base = 0;
+  p.part_tiles = 0;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_m = (int)((M + 127) / 128);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const int nwg = p.tiles_m * p.tiles_n;
+  return epi == 1 ? slab::launch<1, slab::OUT_Y, 2>(p, nwg, stream) : slab::launch<0, slab::OUT_Y, 2>(p, nwg, stream);
 }
 
 hipError_t launch_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K, const uint8_t* wq,

@@ -37,6 +37,12 @@ hipError_t launch_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, i
                               const uint8_t* wq, const uint8_t* ws, int64_t N,
                               const void* bias, int epi, void* y, hipStream_t stream);
 
+// The same GEMM on 256 (weights) x 128 (tokens) tiles: twice the tiles of
+// launch_linear_slab for the same shape, the same result bit for bit.
+hipError_t launch_linear_slab_m128(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                                   const uint8_t* wq, const uint8_t* ws, int64_t N,
+                                   const void* bias, int epi, void* y, hipStream_t stream);
+
 // The slab GEMM writing, instead of y, the MX quantization of bf16 y in the
 // slab layout with rows M and K' = N: hq [N/64][RM][64], hs [N/64][RM][2],
 // RM = slab_rows(M). N % 64 == 0 and RM * N < 2^31.

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mx_abi_version() == 11
+    assert L.mx_abi_version() == 12
     assert L.mx_status_string(0) == b"MX_OK"
     assert L.mx_status_string(1) == b"MX_ERR_INVALID_ARGUMENT"
     assert L.mx_status_string(2) == b"MX_ERR_UNSUPPORTED"
@@ -137,6 +137,12 @@ def test_slab_calls_reject_bad_arguments(L):
     assert lsl(xs=C + 2) == 1  # scales 4-byte aligned
     assert lsl(xq=0) == 1
     assert lsl(y=A + 8192) == 1  # y overlaps the token slab (256 rows x 64 B)
+    assert lsl(N=264) == 2
+    assert lsl(M=0) == 0 and lsl(N=0) == 0
+    # The 128-token-tile form takes the same arguments and checks.
+    ls = L.mx_linear_slab_m128
+    assert lsl(K=96) == 1 and lsl(epi=3) == 1 and lsl(xs=C + 2) == 1 and lsl(xq=0) == 1
+    assert lsl(y=A + 8192) == 1 and lsl(y=D + 8) == 1 and lsl(y=0) == 1
     assert lsl(N=264) == 2
     assert lsl(M=0) == 0 and lsl(N=0) == 0
     rq = L.mx_linear_slab_requant
@@ -332,7 +338,9 @@ def test_per_shape_plan():
 
     assert pkg.plan_linear(128, 5120, 5120) == ("small", 3)
     assert pkg.plan_linear(256, 5120, 5120) == ("small", 1)
-    assert pkg.plan_linear(512, 5120, 10240) == ("splitk", 3)
+    assert pkg.plan_linear(512, 5120, 10240) == ("slab_m128", 1)
+    assert pkg.plan_linear(512, 1024, 1024) == ("splitk", 8)  # 8 tiles: too few for one round of 128-token tiles
+    assert pkg.plan_linear(1024, 5120, 15360) == ("slab", 1)  # 240 tiles
     assert pkg.plan_linear(75348, 5120, 15360) == ("slab", 1)
     assert pkg.plan_ws_bytes(("small", 3), 128, 5120) == 3 * 128 * 5120 * 4
     assert pkg.plan_ws_bytes(("small", 1), 128, 5120) == 0
@@ -350,11 +358,16 @@ def test_plan_entry_points_host_side(L):
         st = L.mx_linear_plan_default(M, K, N, ctypes.byref(kind), ctypes.byref(splits))
         return st, kind.value, splits.value
 
-    # The rule: few-token kernel up to 256 tokens, split-K while the 256 x 256
-    # tiles are fewer than the CUs (256 assumed without a GPU), else slab.
+    # The rule: few-token kernel up to 256 tokens; 128-token tiles when the
+    # 256 x 256 tiles number 32 to 128; split-K while they are fewer than the
+    # CUs (256 assumed without a GPU); else slab.
     assert default(128, 5120, 5120) == (0, 2, 3)
     assert default(256, 5120, 5120) == (0, 2, 1)
-    assert default(512, 5120, 10240) == (0, 1, 3)
+    assert default(512, 5120, 10240) == (0, 4, 1)
+    assert default(300, 5120, 5120) == (0, 4, 1)  # 40 tiles
+    assert default(300, 5120, 3840) == (0, 1, 8)  # 30 tiles: split-K
+    assert default(2048, 5120, 4096) == (0, 4, 1)  # 128 tiles
+    assert default(2048, 5120, 4352) == (0, 0, 1)  # 136 tiles: split-K would be 1
     assert default(75348, 5120, 15360) == (0, 0, 1)
     assert default(0, 64, 64) == (0, 0, 1)  # empty: nothing to split
     assert default(8, 96, 64)[0] == 1 and default(-1, 64, 64)[0] == 1
@@ -365,6 +378,8 @@ def test_plan_entry_points_host_side(L):
     assert L.mx_linear_plan_ws_bytes(1, 3, 512, 5120, 10240) == L.mx_linear_splitk_ws_bytes(512, 10240, 3)
     assert L.mx_linear_plan_ws_bytes(2, 3, 128, 5120, 5120) == 3 * 128 * 5120 * 4
     assert L.mx_linear_plan_ws_bytes(3, 1, 75348, 5120, 5120) == L.mx_linear_balanced_ws_bytes(75348, 5120, 5120)
+    assert L.mx_linear_plan_ws_bytes(4, 1, 512, 5120, 10240) == 0
+    assert L.mx_linear_plan_ws_bytes(4, 2, 512, 5120, 10240) == -1  # 128-token tiles take splits 1
     assert L.mx_linear_plan_ws_bytes(7, 1, 8, 64, 64) == -1
     # The tuner's workspace covers its largest candidate: at 128 x 5120 x 5120
     # split-K with 8 ranges (8 x 20 partial tiles of 256 KiB).
@@ -375,6 +390,8 @@ def test_plan_entry_points_host_side(L):
     assert L.mx_linear_slab_plan(9, 1, P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20,
                                  P(0)) == 1
     assert L.mx_linear_slab_plan(0, 2, P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20,
+                                 P(0)) == 1
+    assert L.mx_linear_slab_plan(4, 2, P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20,
                                  P(0)) == 1
     assert L.mx_linear_tune(P(A), P(B), 8, 256, P(C), P(C + (1 << 20)), 256, P(0), 0, P(D), P(E), 1 << 20, 0, P(0),
                             ctypes.byref(kind), ctypes.byref(splits)) == 1  # reps 0

@@ -32,7 +32,7 @@ def _graph(fn):
 @pytest.mark.parametrize(
     "M,K,N,plan,gelu",
     [(512, 256, 1024, ("slab", 1), False), (300, 320, 272, ("splitk", 3), True), (128, 512, 512, ("small", 2), False),
-     (77, 192, 256, ("small", 1), True)],
+     (77, 192, 256, ("small", 1), True), (300, 320, 528, ("slab_m128", 1), True)],
 )
 def test_graph_replays_match_eager(M, K, N, plan, gelu):
     print(f"graph M={M} K={K} N={N} plan={plan}", flush=True)

@@ -69,7 +69,7 @@ def operands():
     return x, w, b, ref
 
 
-@pytest.mark.parametrize("plan", [("slab", 1), ("splitk", 3), ("small", 1), ("small", 4), ("balanced", 1)])
+@pytest.mark.parametrize("plan", [("slab", 1), ("splitk", 3), ("small", 1), ("small", 4), ("balanced", 1), ("slab_m128", 1)])
 @pytest.mark.parametrize("gelu", [False, True])
 def test_slab_kernels_write_exactly_y(operands, plan, gelu):
     print(f"guard {plan} gelu={gelu}", flush=True)

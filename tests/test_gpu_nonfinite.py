@@ -62,7 +62,7 @@ def expect_nan_lines(yref, x, w):
     assert np.array_equal(np.isnan(yref), bad_m[:, None] | bad_n[None, :])
 
 
-PLANS = [("slab", 1), ("splitk", 3), ("small", 1), ("small", 3), ("balanced", 1)]
+PLANS = [("slab", 1), ("splitk", 3), ("small", 1), ("small", 3), ("balanced", 1), ("slab_m128", 1)]
 
 
 @pytest.mark.parametrize("plan", PLANS, ids=[f"{k}{s}" for k, s in PLANS])

@@ -28,7 +28,8 @@ def oracle_linear(x, w, b, gelu):
 
 CASES = [
     # M, K, N, gelu, bias: the default plan is the few-token kernel with
-    # several K ranges up to 256 tokens, split-K or the slab GEMM above.
+    # several K ranges up to 256 tokens; above, the 128-token tiles (640 x
+    # 512 x 4096: 48 tiles of 256 x 256), split-K or the slab GEMM.
     (128, 5120, 5120, False, True),
     (77, 640, 272, True, True),
     (200, 256, 512, False, False),
@@ -36,6 +37,7 @@ CASES = [
     (256, 13824, 1024, False, True),
     (300, 512, 768, True, True),
     (1000, 512, 512, False, True),
+    (640, 512, 4096, True, False),
 ]
 
 
