@@ -649,7 +649,7 @@ def main():
         wqa = mean(wq_per[0])
         ws_buf = torch.empty((mx.mx_linear_ws_bytes(M, K, N),), dtype=torch.uint8, device=dev)
         one_call = lambda: mx.mx_linear(x, wsl, bias, y=y, workspace=ws_buf)  # noqa: E731
-        oc_total, _ = timed_step(torch, [one_call], 10, 2)
+        oc_total, _ = timed_step(torch, [one_call], 30, 5)
         del ws_buf
         rm_total, (rq_ms, rg_ms) = timed_step(torch, rowmajor, 10, 2)
         _, (f_ms,) = timed_step(torch, [fused], 10, 2)
@@ -666,7 +666,7 @@ def main():
             "gemm_ms_p10_p50_p90": percentiles(g_ms),
             "step_ms_p10_p50_p90": percentiles([a + b for a, b in zip(q_ms, g_ms)]),
             "cold": cold,
-            "mx_linear_one_call_ms": round(oc_total / 10, 4),
+            "mx_linear_one_call_ms": round(oc_total / 30, 4),
             "rowmajor_step_ms": round(rm_total / 10, 4),
             "rowmajor_step_TFLOPs": round(flop / (rm_total / 10 * 1e-3) / 1e12, 2),
             "rowmajor_gemm_ms": round(mean(rg_ms), 4),

@@ -76,6 +76,7 @@ __device__ inline float quotient_fma(float v, float scale, float rinv) {
 // Codes of 8 elements under the row's scale, packed 8 bytes. `fast` and
 // `rinv` are the row's (scale >= 2^-100 and finite; RN(1 / scale)).
 __device__ inline uint2 encode8(const float v[8], float scale, float rinv, bool fast, bool bad) {
+  if (bad) return uint2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
   float t[8];
   if (fast) {
 #pragma unroll
@@ -84,11 +85,20 @@ __device__ inline uint2 encode8(const float v[8], float scale, float rinv, bool 
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = scale == 0.f ? __builtin_copysignf(0.f, v[i]) : v[i] / scale;
   }
-  uint32_t code[8];
+  // The hardware conversion rounds to nearest even onto the E4M3 grid
+  // (subnormals included, the sign of zero kept). Clamping to +-448 first
+  // gives the saturated result: every value between 448 and 464 rounds to
+  // 448 anyway, and 464 is a tie that goes to 448's even significand.
+  int w[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) code[i] = bad ? 0x7Fu : e4m3_from_scaled_f32(t[i]);
-  return uint2{code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-               code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24)};
+  for (int h = 0; h < 2; ++h) {
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(t[4 * h + i], -448.0f, 448.0f);
+    w[h] = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w[h] = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w[h], true);
+  }
+  return uint2{(uint32_t)w[0], (uint32_t)w[1]};
 }
 
 // The row's scale from the lanes' partial maxima of magnitude bits.
