@@ -119,6 +119,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restri
 // 16 or 32 rows the same as that order there, though faster at K = 13824).
 constexpr int kTileRows = 8, kTileK = 512;
 constexpr int kTileItems = kTileRows / 4;  // 8-element items per thread and tile
+// LDS bytes per slab of the tile: its rows plus 64 bytes of padding, so that
+// the four slabs a half-wave writes at once start 16 banks apart and its 32
+// eight-byte writes cover the 64 banks once.
+constexpr int kSlabLds = kTileRows * 64 + 64;
 static_assert(kTileRows % 8 == 0 && 256 % kTileRows == 0, "tile rows divide the slab row padding");
 
 template <typename Idx>
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void quantize_slab_tiled_kernel(const uin
                                                                        Idx ld, Idx R, Idx tiles_per_block,
                                                                        uint8_t* __restrict__ q,
                                                                        uint8_t* __restrict__ s) {
-  __shared__ __attribute__((aligned(16))) uint8_t lq[8 * kTileRows * 64];  // [slab][row][64]
+  __shared__ __attribute__((aligned(16))) uint8_t lq[8 * kSlabLds];  // [slab][row][64], slabs kSlabLds apart
   __shared__ uint8_t ls[8 * kTileRows * 2];                                // [slab][row][2]
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void quantize_slab_tiled_kernel(const uin
       uint32_t codes[2], sc;
       quantize8_bf16(raw[j], codes, sc);  // every lane: the quads stay whole
       const int row_l = wave + 4 * j;
-      *(i32x2*)(lq + sl_l * (kTileRows * 64) + row_l * 64 + (lane & 7) * 8) = i32x2{(int)codes[0], (int)codes[1]};
+      *(i32x2*)(lq + sl_l * kSlabLds + row_l * 64 + (lane & 7) * 8) = i32x2{(int)codes[0], (int)codes[1]};
       if ((lane & 3) == 0) ls[sl_l * (kTileRows * 2) + row_l * 2 + ((lane >> 2) & 1)] = (uint8_t)sc;
     }
     __syncthreads();
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void quantize_slab_tiled_kernel(const uin
         uint8_t* srun = s + (size_t)(gs * R * 2 + r0 * 2);
 #pragma unroll
         for (int i = 0; i < kTileRows / 8; ++i)
-          *(i32x4*)(qrun + (piece + 32 * i) * 16) = *(const i32x4*)(lq + sl * (kTileRows * 64) + (piece + 32 * i) * 16);
+          *(i32x4*)(qrun + (piece + 32 * i) * 16) = *(const i32x4*)(lq + sl * kSlabLds + (piece + 32 * i) * 16);
 #pragma unroll
         for (int i = 0; i < (2 * kTileRows + 31) / 32; ++i)
           if (piece + 32 * i < 2 * kTileRows) srun[piece + 32 * i] = ls[sl * (kTileRows * 2) + piece + 32 * i];
