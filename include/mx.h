@@ -340,7 +340,11 @@ void mx_linear_plan_clear(void);
  * past the limits). */
 int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N);
 
-/* x bf16 [M][ldx] (ldx >= K, ldx % 8 == 0) is quantized into `workspace`
+/* The whole quantized linear in one call: the activations quantized to MXFP8
+ * at run time, then the block-scaled product with the stored MXFP8 weights
+ * (model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details"). This is the production entry point.
+ * x bf16 [M][ldx] (ldx >= K, ldx % 8 == 0) is quantized into `workspace`
  * (mx_quantize_act_slab's layout), then multiplied by the slab weights
  * wq [K/64][RN][64], ws [K/64][RN][2] (mx_quantize_weight_slab or
  * mx_slab_pack) with bias (f16 [N] or NULL) and epilogue into y bf16 [M][N],
@@ -350,8 +354,8 @@ int64_t mx_linear_ws_bytes(int64_t M, int64_t K, int64_t N);
  * quantizer, then the GEMM), plus the ordered reduction of the partial sums
  * for plans with several K ranges. Nothing is allocated. workspace: device
  * memory of mx_linear_ws_bytes(M, K, N) bytes (at least what the chosen
- * plan needs), 256-byte aligned, not overlapping x, the weights, bias or y; its contents
- * are overwritten and need no initial value. K % 64 == 0, N % 16 == 0.
+ * plan needs), 256-byte aligned, not overlapping x, the weights, bias or y;
+ * its contents are overwritten and need no initial value. K % 64 == 0, N % 16 == 0.
  * Results: deterministic; bit-identical to mx_quantize_act_slab +
  * mx_linear_slab_plan with the same plan. Errors: as mx_linear_slab, plus
  * MX_ERR_INVALID_ARGUMENT for a bad pitch, a short or misplaced workspace. */
