@@ -107,13 +107,17 @@ int mx_quantize_weight(const void* w, int wdtype, int64_t N, int64_t K, int64_t 
  * but slow: every 256 x 256 tile quantizes its bf16 token rows again, and the
  * kernel holds them beside 256 accumulators per lane and spills (about 760
  * TFLOP/s at 75348 x 5120 x 15360, against about 2600 for mx_linear). Kept
- * for callers without slab weights or workspace. */
+ * for callers without slab weights or workspace.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details" (activations quantized at run time). */
 int mx_linear_fused(const void* x, int64_t M, int64_t K,
                     const uint8_t* wq, const uint8_t* ws, int64_t N,
                     const void* bias, int epilogue, void* y, void* stream);
 
 /* The same linear on activations already quantized (e.g. by
- * mx_quantize_act): xq: uint8 [M][K], xs: uint8 [M][K/32]. */
+ * mx_quantize_act): xq: uint8 [M][K], xs: uint8 [M][K/32].
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details". */
 int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                 const uint8_t* wq, const uint8_t* ws, int64_t N,
                 const void* bias, int epilogue, void* y, void* stream);
@@ -134,17 +138,23 @@ int mx_linear_q(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
 int64_t mx_slab_rows(int64_t rows);
 
 /* mx_quantize_act writing the slab layout. K % 64 == 0; q: uint8
- * [K/64][R][64], s: uint8 [K/64][R][2] with R = mx_slab_rows(M). */
+ * [K/64][R][64], s: uint8 [K/64][R][2] with R = mx_slab_rows(M).
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details" (dynamic MXFP8 activations). */
 int mx_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx,
                          uint8_t* q, uint8_t* s, void* stream);
 
-/* mx_quantize_weight writing the slab layout (R = mx_slab_rows(N)). */
+/* mx_quantize_weight writing the slab layout (R = mx_slab_rows(N)).
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details" (E4M3 weights, one E8M0 scale per 32). */
 int mx_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
                             uint8_t* q, uint8_t* s, void* stream);
 
 /* Row-major codes q [rows][K] and scales s [rows][K/32] (e.g. weights that
  * were stored quantized) to the slab layout qslab, sslab. K % 64 == 0; codes
- * 16-byte aligned, scales 2-byte aligned; outputs must not overlap inputs. */
+ * 16-byte aligned, scales 2-byte aligned; outputs must not overlap inputs.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details" (weights stored quantized). */
 int mx_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
                  uint8_t* qslab, uint8_t* sslab, void* stream);
 
@@ -153,7 +163,9 @@ int mx_slab_pack(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
  * (RN = mx_slab_rows(N)); bias f16 [N] or NULL; y bf16 [M][N] row-major.
  * K % 64 == 0 (else MX_ERR_INVALID_ARGUMENT), N % 16 == 0 (else
  * MX_ERR_UNSUPPORTED); codes and y 16-byte aligned, scales 4-byte aligned.
- * The result is bit-identical to mx_linear_q on the same codes and scales. */
+ * The result is bit-identical to mx_linear_q on the same codes and scales.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details". */
 int mx_linear_slab(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                    const uint8_t* wq, const uint8_t* ws, int64_t N,
                    const void* bias, int epilogue, void* y, void* stream);
@@ -179,7 +191,10 @@ int mx_linear_slab_m128(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t
  * then ffn.net.2 on the requantized intermediate) without the bf16
  * intermediate in memory. N % 64 == 0 (else MX_ERR_INVALID_ARGUMENT);
  * RM * N < 2^31 (else MX_ERR_UNSUPPORTED); hq 16-byte aligned; outputs must
- * not overlap the inputs or each other. */
+ * not overlap the inputs or each other.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details" (ffn.net.0.proj and ffn.net.2 are both
+ * quantized linears). */
 int mx_linear_slab_requant(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                            const uint8_t* wq, const uint8_t* ws, int64_t N,
                            const void* bias, int epilogue, uint8_t* hq, uint8_t* hs, void* stream);
@@ -211,7 +226,10 @@ int mx_linear_splitk_choose(int64_t M, int64_t K, int64_t N);
  * (else MX_ERR_UNSUPPORTED). workspace: device memory of at least
  * mx_linear_splitk_ws_bytes(M, N, splits) bytes, 256-byte aligned, not
  * overlapping the operands, bias or y; overwritten. Two kernels on `stream`;
- * nothing is allocated. */
+ * nothing is allocated.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details"; ragged token counts as in "Wan2.2 I2V A14B,
+ * four-step 720p: native LightX2V FP8 and NVFP4", section "Runtime setup". */
 int mx_linear_slab_splitk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                           const uint8_t* wq, const uint8_t* ws, int64_t N,
                           const void* bias, int epilogue, void* y, int splits,
@@ -245,7 +263,10 @@ int mx_linear_small_choose(int64_t M, int64_t K, int64_t N);
  * MX_ERR_UNSUPPORTED). workspace: at least mx_linear_small_ws_bytes(M, N,
  * splits) bytes, 256-byte aligned, not overlapping an operand, bias or y; may
  * be NULL when that is 0; overwritten. One or two kernels on `stream`;
- * nothing is allocated. */
+ * nothing is allocated.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details"; ragged token counts as in "Wan2.2 I2V A14B,
+ * four-step 720p: native LightX2V FP8 and NVFP4", section "Runtime setup". */
 int mx_linear_slab_small(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                          const uint8_t* wq, const uint8_t* ws, int64_t N,
                          const void* bias, int epilogue, void* y, int splits,
@@ -278,7 +299,9 @@ int mx_linear_plan_default(int64_t M, int64_t K, int64_t N, int* kind, int* spli
 int64_t mx_linear_plan_ws_bytes(int kind, int splits, int64_t M, int64_t K, int64_t N);
 
 /* mx_linear_slab through the given plan: the arguments, checks and errors of
- * that plan's entry point (workspace unused by MX_PLAN_SLAB). */
+ * that plan's entry point (workspace unused by MX_PLAN_SLAB).
+ * Passage: per-shape kernel choice, "Model Quantization Techniques", section
+ * "MiniMax-H3 FP8 with FP16 Accumulation". */
 int mx_linear_slab_plan(int kind, int splits, const uint8_t* xq, const uint8_t* xs,
                         int64_t M, int64_t K, const uint8_t* wq, const uint8_t* ws,
                         int64_t N, const void* bias, int epilogue, void* y,
@@ -301,7 +324,9 @@ int64_t mx_linear_tune_ws_bytes(int64_t M, int64_t K, int64_t N);
  * device, M, K, N, epilogue) and written to *kind, *splits. y is
  * overwritten; the stream is synchronized (not for use under graph
  * capture). Errors: those of the slab linear's checks, MX_ERR_INVALID_ARGUMENT
- * when no candidate fits the workspace, MX_ERR_HIP from the runs. */
+ * when no candidate fits the workspace, MX_ERR_HIP from the runs.
+ * Passage: per-shape tuning at warm-up, "Model Quantization Techniques",
+ * section "MiniMax-H3 FP8 with FP16 Accumulation". */
 int mx_linear_tune(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                    const uint8_t* wq, const uint8_t* ws, int64_t N,
                    const void* bias, int epilogue, void* y,
@@ -314,7 +339,9 @@ int mx_linear_plan_lookup(int64_t M, int64_t K, int64_t N, int epilogue, int* ki
 
 /* mx_linear_slab through mx_linear_plan_lookup's plan. workspace: at least
  * mx_linear_plan_ws_bytes of that plan (mx_linear_tune_ws_bytes always
- * suffices); may be NULL when the plan needs none. Nothing is allocated. */
+ * suffices); may be NULL when the plan needs none. Nothing is allocated.
+ * Passage: per-shape tuning at warm-up, "Model Quantization Techniques",
+ * section "MiniMax-H3 FP8 with FP16 Accumulation". */
 int mx_linear_slab_auto(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                         const uint8_t* wq, const uint8_t* ws, int64_t N,
                         const void* bias, int epilogue, void* y,
@@ -420,7 +447,9 @@ int64_t mx_linear_balanced_ws_bytes(int64_t M, int64_t K, int64_t N);
  * mx_linear_balanced_ws_bytes(M, K, N) bytes, 256-byte aligned, not
  * overlapping an operand, bias or y (may be NULL when that is 0). Up to three
  * kernels on `stream`; nothing is allocated. Other arguments and errors as
- * mx_linear_slab. */
+ * mx_linear_slab.
+ * Passage: model card "Wan2.2-I2V-A14B-Lightning · MXFP8 (AutoRound OptRTN)",
+ * section "Quantization Details". */
 int mx_linear_slab_balanced(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                             const uint8_t* wq, const uint8_t* ws, int64_t N,
                             const void* bias, int epilogue, void* y,
@@ -453,7 +482,9 @@ int mx_pc_quantize_act_slab(const void* x, int64_t M, int64_t K, int64_t ldx,
 
 /* Per-output-channel quantization of weights w [N][ldw] of type wdtype
  * (MX_DT_F32 or MX_DT_BF16; ldw * sizeof(element) % 16 == 0): q uint8
- * [K/64][RN][64], s f32 [RN]. */
+ * [K/64][RN][64], s f32 [RN].
+ * Passage: "Wan2.2 I2V A14B, four-step 720p: native LightX2V FP8 and NVFP4",
+ * section "Conversion and compatibility". */
 int mx_pc_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, int64_t ldw,
                                uint8_t* q, float* s, void* stream);
 
@@ -464,7 +495,10 @@ int mx_pc_quantize_weight_slab(const void* w, int wdtype, int64_t N, int64_t K, 
  * with unit scales; the row scales are applied to the f32 sums). Operands in
  * the layout above; bias f16 [N] or NULL; y bf16 [M][N]. K % 64 == 0, N % 16
  * == 0 (else MX_ERR_UNSUPPORTED); codes and y 16-byte aligned, scales 4-byte
- * aligned; y must not overlap an input. */
+ * aligned; y must not overlap an input.
+ * Passage: "Wan2.2 I2V A14B, four-step 720p: native LightX2V FP8 and NVFP4",
+ * section "Conversion and compatibility"; FP32 accumulation as in "Model
+ * Quantization Techniques", mode table. */
 int mx_pc_linear_slab(const uint8_t* xq, const float* xs, int64_t M, int64_t K,
                       const uint8_t* wq, const float* ws, int64_t N,
                       const void* bias, int epilogue, void* y, void* stream);
