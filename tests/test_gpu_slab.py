@@ -53,7 +53,11 @@ def slab_rows_of(sl, rows):
     return q.transpose(1, 0, 2).reshape(n, -1), s.transpose(1, 0, 2).reshape(n, -1)
 
 
-@pytest.mark.parametrize("M,K", [(1, 64), (77, 192), (256, 128), (300, 5120), (513, 640)])
+# The bf16 slab quantizer works on 8-row x 512-K tiles: shapes on and around
+# those edges (partial last K tile, rows just under and over a tile, a pad
+# region inside the last tile) are compared whole, pad rows included.
+@pytest.mark.parametrize("M,K", [(1, 64), (77, 192), (256, 128), (300, 5120), (513, 640), (7, 512), (8, 448),
+                                 (9, 576), (255, 1024), (257, 1088)])
 def test_act_slab_quantizer_matches_oracle(M, K):
     x = synth.make_activation(M, K, seed=M + 3 * K)
     sl = mx().mx_quantize_act_slab(x.to(dev()))
