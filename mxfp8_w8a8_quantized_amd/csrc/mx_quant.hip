@@ -125,6 +125,7 @@ constexpr int kTileItems = kTileRows / 4;  // 8-element items per thread and til
 // eight-byte writes cover the 64 banks once.
 constexpr int kSlabLds = kTileRows * 64 + 64;
 static_assert(kTileRows % 8 == 0 && 256 % kTileRows == 0, "tile rows divide the slab row padding");
+static_assert((kSlabLds / 4) % 64 == 16, "consecutive slabs of the tile start 16 LDS banks apart");
 
 template <typename Idx>
 __global__ __launch_bounds__(kThreads) void quantize_slab_tiled_kernel(const uint16_t* __restrict__ x, Idx rows, Idx K,
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void quantize_slab_tiled_kernel(const uin
                                                                        uint8_t* __restrict__ q,
                                                                        uint8_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) uint8_t lq[8 * kSlabLds];  // [slab][row][64], slabs kSlabLds apart
-  __shared__ uint8_t ls[8 * kTileRows * 2];                                // [slab][row][2]
+  __shared__ uint8_t ls[8 * kTileRows * 2];                           // [slab][row][2]
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int sl_l = lane >> 3;  // the lane's slab within the tile
