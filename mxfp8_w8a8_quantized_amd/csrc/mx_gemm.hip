@@ -42,6 +42,8 @@
 // load as zero and their stores are dropped.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -1059,24 +1061,42 @@ __device__ __forceinline__ void store_tile_q(const f32x16 (&acc)[4][4], const Pa
   const int ng = n0 + wn * 128 + 8 * c;  // K' index of this lane's first value
   const bool n_ok = ng < p.N;
   const int slab = ng >> 6;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int row = 4 * it + (lane >> 4);
-    const int mg = m0 + wm * 128 + row;
-    const int sw = row & 31;
-    i32x4 v = *(const i32x4*)(ep + row * 256 + ((((2 * c) ^ sw) & ~1) << 3));
-    if (sw & 1) v = i32x4{v[2], v[3], v[0], v[1]};
-    if (mg >= p.M) v = i32x4{0, 0, 0, 0};
-    const uint32_t raw[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-    uint32_t codes[2], sc;
-    quantize8_bf16(raw, codes, sc);
-    const int qo = n_ok ? slab * RM * 64 + mg * 64 + (ng & 63) : kDropOffset;
-    __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)codes[0], (int)codes[1]}, rq, qo, 0, 0);
-    if ((c & 3) == 0) {
-      const int so = n_ok ? slab * RM * 2 + mg * 2 + ((c >> 2) & 1) : kDropOffset;
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rs, so, 0, 0);
+  // Eight rows' staging reads are issued together before their codes are
+  // computed (one read at a time left each waiting out the LDS latency), and
+  // the pad-row check is compiled in only for a tile that reaches past M:
+  // 1.5% off the GELU up-projection at 75348 x 5120 x 13824, same bytes.
+  auto rows8 = [&](auto tail_c) {
+    constexpr bool TAIL = decltype(tail_c)::value;
+    for (int g = 0; g < 32; g += 8) {
+      i32x4 vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int row = 4 * (g + u) + (lane >> 4);
+        vv[u] = *(const i32x4*)(ep + row * 256 + ((((2 * c) ^ (row & 31)) & ~1) << 3));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int row = 4 * (g + u) + (lane >> 4);
+        const int mg = m0 + wm * 128 + row;
+        i32x4 v = vv[u];
+        if (row & 1) v = i32x4{v[2], v[3], v[0], v[1]};
+        if (TAIL && mg >= p.M) v = i32x4{0, 0, 0, 0};
+        const uint32_t raw[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+        uint32_t codes[2], sc;
+        quantize8_bf16(raw, codes, sc);
+        const int qo = n_ok ? slab * RM * 64 + mg * 64 + (ng & 63) : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)codes[0], (int)codes[1]}, rq, qo, 0, 0);
+        if ((c & 3) == 0) {
+          const int so = n_ok ? slab * RM * 2 + mg * 2 + ((c >> 2) & 1) : kDropOffset;
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rs, so, 0, 0);
+        }
+      }
     }
-  }
+  };
+  if (m0 + wm * 128 + 128 > p.M)
+    rows8(std::integral_constant<bool, true>{});
+  else
+    rows8(std::integral_constant<bool, false>{});
 }
 
 // Split-K output: the wave's fp32 accumulators as they sit in registers,
