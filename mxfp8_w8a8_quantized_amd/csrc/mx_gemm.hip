@@ -484,6 +484,14 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Bi
                                             uint8_t* ep, int m0, int n0, int rows_m, int rows_n, int wn, int wm,
                                             int lane, const float* tab = nullptr) {
   const int r32 = lane & 31, hi = lane >> 5;
+  // Per-channel output: the lane's token-row scales are read once, ahead of
+  // the staging writes (read between them, each read waited out its own LDS
+  // latency).
+  float sx[MF];
+  if constexpr (PC) {
+#pragma unroll
+    for (int j = 0; j < MF; ++j) sx[j] = tab[256 + wm * 32 * MF + 32 * j + r32];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -499,7 +507,7 @@ __device__ __forceinline__ void store_tile8(const f32x16 (&acc)[4][MF], const Bi
         const int m = 32 * j + r32;
         float v[4];
         if constexpr (PC) {
-          const float sxm = tab[256 + wm * 32 * MF + m];
+          const float sxm = sx[j];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = epilogue<EPI>(acc[i][j][4 * q + r] * (sxm * swq[r]) + b[r]);
         } else if constexpr (BIAS_IN_ACC) {
